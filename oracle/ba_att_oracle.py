@@ -333,6 +333,12 @@ def _softmax_attention(x_logits: np.ndarray, v: np.ndarray):
     return O, lse[:, 0]
 
 
+def _kept_keys(mask_row: np.ndarray, b: int, N: int) -> np.ndarray:
+    """Token indices t < N of the key blocks kept in one mask row."""
+    parts = [np.arange(J * b, min((J + 1) * b, N)) for J in range(len(mask_row)) if mask_row[J]]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
 def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
                     b: int, scale: float):
     """Block-sparse attention for one head (reading R6).
@@ -340,7 +346,9 @@ def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarra
     [BA-Att review, "The pith"]: attention is computed only over the kept
     blocks.  For every valid query s of block I the logits scale*<q_s, k_t>
     run over the tokens t < N of the key blocks J with mask[I, J] == 1.
-    Returns O [N, D] and LSE [N] (natural log, scale included).
+    Returns O [N, D] and LSE [N] (natural log, scale included).  A row whose
+    mask keeps no block has an empty key set: the empty sum gives O = 0 and
+    LSE = ln 0 = -inf.
     """
     N = q.shape[0]
     n = num_blocks(N, b)
@@ -348,8 +356,10 @@ def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarra
     lse = np.zeros(N)
     for I in range(n):
         rows = np.arange(I * b, min((I + 1) * b, N))
-        keys = np.concatenate([np.arange(J * b, min((J + 1) * b, N))
-                               for J in range(n) if mask[I, J]])
+        keys = _kept_keys(mask[I], b, N)
+        if keys.size == 0:
+            O[rows], lse[rows] = 0.0, -np.inf
+            continue
         X = scale * (q[rows] @ k[keys].T)
         O[rows], lse[rows] = _softmax_attention(X, v[keys])
     return O, lse
@@ -360,14 +370,15 @@ def block_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.n
     """Block-sparse attention for a chosen subset of query rows only (same
     definition as `block_attention`); used for sampled parity at full size."""
     N = q.shape[0]
-    n = num_blocks(N, b)
     rows = np.asarray(rows, dtype=np.int64)
     O = np.zeros((rows.size, v.shape[1]))
     lse = np.zeros(rows.size)
     for i, s in enumerate(rows):
         I = int(s) // b
-        keys = np.concatenate([np.arange(J * b, min((J + 1) * b, N))
-                               for J in range(n) if mask[I, J]])
+        keys = _kept_keys(mask[I], b, N)
+        if keys.size == 0:
+            O[i], lse[i] = 0.0, -np.inf
+            continue
         X = scale * (q[s:s + 1] @ k[keys].T)
         O[i:i + 1], lse[i:i + 1] = _softmax_attention(X, v[keys])
     return O, lse

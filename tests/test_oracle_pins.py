@@ -449,3 +449,15 @@ def test_planted_dropped_variance_product_fails_zero_mean_pin():
     bad = oracle_pair_score(Xq, Xk, scale, score=_score_without_vv)
     assert abs((good - exact) / lead - 1) < 0.02
     assert abs((bad - exact) / lead - 1) > 10
+
+
+def test_empty_mask_row_is_the_empty_sum():
+    N, b, D = 48, 16, 4
+    q, k, v = _rand_head(N, D, 8)
+    mask = np.ones((3, 3), np.uint8)
+    mask[1] = 0
+    O, lse = orc.block_attention(q, k, v, mask, b, 0.5)
+    assert np.all(O[16:32] == 0) and np.all(np.isneginf(lse[16:32]))
+    assert np.all(np.isfinite(lse[:16])) and np.all(np.isfinite(lse[32:]))
+    Or, lr = orc.block_attention_rows(q, k, v, mask, b, 0.5, [3, 20])
+    assert np.all(Or[1] == 0) and np.isneginf(lr[1]) and np.allclose(Or[0], O[3])
