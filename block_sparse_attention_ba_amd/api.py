@@ -1,0 +1,176 @@
+"""Python binding of the gfx950 BA-Att library.
+
+Argument marshalling only: every step of the operator runs in the HIP
+kernels behind the C ABI (include/ba_att.h).  torch supplies device memory
+and the current stream; tensors must already live on the GPU.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+BA_BF16, BA_F32 = 0, 1
+
+__all__ = [
+    "load", "num_blocks", "keep_count", "select_workspace_bytes", "select", "mask_to_index",
+    "forward", "dense", "ba_attention",
+]
+
+
+def load():
+    return _lib.load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = _lib.load().ba_att_status_string(status).decode()
+        raise RuntimeError(f"BA-Att call failed: {msg} (status {status})")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def num_blocks(N: int, block: int) -> int:
+    return int(_lib.load().ba_att_num_blocks(N, block))
+
+
+def keep_count(n_blocks: int, sparsity: float) -> int:
+    return int(_lib.load().ba_att_keep_count(n_blocks, float(sparsity)))
+
+
+def select_workspace_bytes(B: int, H: int, N: int, D: int, block: int) -> int:
+    return int(_lib.load().ba_att_select_workspace_bytes(B, H, N, D, block))
+
+
+def _qkv_shape(q: torch.Tensor):
+    _need(q, "q", torch.bfloat16, 4)
+    return tuple(int(x) for x in q.shape)
+
+
+def select(q: torch.Tensor, k: torch.Tensor, block: int, sparsity: float, scale: float | None = None,
+           return_score: bool = False, workspace: torch.Tensor | None = None):
+    """Selection pass: returns (mask uint8 [B,H,n,n], idx int32 [B,H,n,keep],
+    cnt int32 [B,H,n]) and, with return_score, the fp32 score map."""
+    B, H, N, D = _qkv_shape(q)
+    _need(k, "k", torch.bfloat16, 4)
+    if tuple(k.shape) != (B, H, N, D):
+        raise ValueError("q and k must have the same shape")
+    lib = _lib.load()
+    n = num_blocks(N, block)
+    keep = keep_count(n, sparsity)
+    if keep < 1:
+        raise ValueError("sparsity must lie in [0, 1)")
+    dev = q.device
+    mask = torch.empty((B, H, n, n), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    score = torch.empty((B, H, n, n), dtype=torch.float32, device=dev) if return_score else None
+    need = select_workspace_bytes(B, H, N, D, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib.ba_att_select(B, H, N, D, block, float(scale or 0.0), float(sparsity),
+                             q.data_ptr(), k.data_ptr(), mask.data_ptr(), idx.data_ptr(),
+                             cnt.data_ptr(), score.data_ptr() if score is not None else None,
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream(q)))
+    if return_score:
+        return mask, idx, cnt, score
+    return mask, idx, cnt
+
+
+def mask_to_index(mask: torch.Tensor, max_keep: int | None = None):
+    """Block mask uint8 [B,H,n,n] -> (idx int32 [B,H,n,max_keep], cnt int32 [B,H,n])."""
+    _need(mask, "mask", torch.uint8, 4)
+    B, H, n, n2 = (int(x) for x in mask.shape)
+    if n != n2:
+        raise ValueError("mask must be square in its last two dimensions")
+    max_keep = n if max_keep is None else int(max_keep)
+    idx = torch.empty((B, H, n, max_keep), dtype=torch.int32, device=mask.device)
+    cnt = torch.empty((B, H, n), dtype=torch.int32, device=mask.device)
+    _check(_lib.load().ba_att_mask_to_index(B, H, n, mask.data_ptr(), max_keep, idx.data_ptr(),
+                                            cnt.data_ptr(), _stream(mask)))
+    return idx, cnt
+
+
+def _out(q, out_dtype, out, lse, return_lse):
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    B, H, N, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=out_dtype, device=q.device)
+    else:
+        _need(out, "out", out_dtype, 4)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    code = BA_F32 if out_dtype == torch.float32 else BA_BF16
+    return out, lse, code
+
+
+def forward(q, k, v, idx, cnt, block: int, scale: float | None = None,
+            out_dtype: torch.dtype = torch.float32, out=None, lse=None, return_lse: bool = True):
+    """Block-sparse attention over the listed key blocks; returns (O, LSE)."""
+    B, H, N, D = _qkv_shape(q)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, 4)
+        if tuple(t.shape) != (B, H, N, D):
+            raise ValueError(f"{name} must have the shape of q")
+    _need(idx, "idx", torch.int32, 4)
+    _need(cnt, "cnt", torch.int32, 3)
+    n = num_blocks(N, block)
+    if tuple(idx.shape[:3]) != (B, H, n) or tuple(cnt.shape) != (B, H, n):
+        raise ValueError("idx/cnt must be [B,H,n,max_keep] / [B,H,n]")
+    out, lse, code = _out(q, out_dtype, out, lse, return_lse)
+    _check(_lib.load().ba_att_forward(B, H, N, D, block, float(scale or 0.0), q.data_ptr(),
+                                      k.data_ptr(), v.data_ptr(), idx.data_ptr(), cnt.data_ptr(),
+                                      int(idx.shape[3]), out.data_ptr(), code,
+                                      lse.data_ptr() if lse is not None else None, _stream(q)))
+    return out, lse
+
+
+def dense(q, k, v, scale: float | None = None, out_dtype: torch.dtype = torch.float32,
+          out=None, lse=None, return_lse: bool = True):
+    """Dense attention softmax(scale Q K^T) V; returns (O, LSE)."""
+    B, H, N, D = _qkv_shape(q)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, 4)
+        if tuple(t.shape) != (B, H, N, D):
+            raise ValueError(f"{name} must have the shape of q")
+    out, lse, code = _out(q, out_dtype, out, lse, return_lse)
+    _check(_lib.load().ba_att_dense(B, H, N, D, float(scale or 0.0), q.data_ptr(), k.data_ptr(),
+                                    v.data_ptr(), out.data_ptr(), code,
+                                    lse.data_ptr() if lse is not None else None, _stream(q)))
+    return out, lse
+
+
+def ba_attention(q, k, v, block: int, sparsity: float, scale: float | None = None,
+                 out_dtype: torch.dtype = torch.bfloat16):
+    """Both passes: selection then block-sparse attention; returns (O, LSE, mask)."""
+    mask, idx, cnt = select(q, k, block, sparsity, scale)
+    out, lse = forward(q, k, v, idx, cnt, block, scale, out_dtype=out_dtype)
+    return out, lse, mask
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

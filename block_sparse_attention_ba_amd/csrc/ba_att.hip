@@ -1,0 +1,245 @@
+// C-ABI entry points of the gfx950 BA-Att library (declared in ba_att.h).
+//
+// Host code only validates arguments, carves the caller's workspace and
+// enqueues kernels on the caller's stream.  Nothing is allocated and nothing
+// synchronises the host.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ba_att.h"
+#include "attention.hpp"
+#include "select.hpp"
+
+namespace {
+
+constexpr int kMaxN = 1 << 20;
+constexpr int kMaxBlocksPerRow = 1024;  // mask -> index rows
+constexpr int kMaxSelectBlocks = 512;   // score rows staged in LDS: 16 rows x n fp32
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int num_blocks(int N, int block) { return (N + block - 1) / block; }
+
+// Shape checks shared by every entry point that takes Q/K/V.
+ba_status check_shape(int B, int H, int N, int D) {
+  if (B < 1 || H < 1 || N < 1 || D < 1) return BA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return BA_ERR_UNSUPPORTED;
+  if (N > kMaxN) return BA_ERR_UNSUPPORTED;
+  const long long elems = (long long)B * H * N * D;
+  if (elems >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  return BA_OK;
+}
+
+float resolve_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf((float)D); }
+
+int round_up8(int x) { return (x + 7) / 8 * 8; }
+
+ba_status finish_launch() {
+  return hipGetLastError() == hipSuccess ? BA_OK : BA_ERR_HIP;
+}
+
+int ni_for(int n) {  // elements per lane for a row of n blocks: 1, 2, 4, 8 or 16
+  int ni = 1;
+  while (ni * 64 < n) ni *= 2;
+  return ni;
+}
+
+template <int D>
+void launch_pool(int BH, int N, int n, int block, float scale, const uint16_t* q, const uint16_t* k,
+                 float* aq, float* ak, hipStream_t s) {
+  const dim3 grid(2 * BH * n);
+  if (block == 64)
+    ba::pool_stats_kernel<D, 64><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
+  else
+    ba::pool_stats_kernel<D, 128><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
+}
+
+template <int D, int NI>
+void launch_score_ni(int BH, int n, int keep, const float* aq, const float* ak, uint8_t* mask,
+                     int32_t* idx, int32_t* cnt, float* score, hipStream_t s) {
+  const int tiles = (n + ba::kScoreRows - 1) / ba::kScoreRows;
+  const size_t smem = (size_t)ba::kScoreRows * n * sizeof(float);
+  ba::score_topk_kernel<D, NI><<<dim3(BH * tiles), 256, smem, s>>>(aq, ak, n, keep, mask, idx, cnt, score);
+}
+
+template <int D>
+void launch_score(int BH, int n, int keep, const float* aq, const float* ak, uint8_t* mask,
+                  int32_t* idx, int32_t* cnt, float* score, hipStream_t s) {
+  switch (ni_for(n)) {
+    case 1: launch_score_ni<D, 1>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
+    case 2: launch_score_ni<D, 2>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
+    case 4: launch_score_ni<D, 4>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
+    case 8: launch_score_ni<D, 8>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
+    default: launch_score_ni<D, 16>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
+  }
+}
+
+template <int D, int WAVES, int BLK, bool SPARSE>
+void launch_attn(const ba::AttnParams& p, bool out_f32, hipStream_t s) {
+  const dim3 grid(round_up8(p.total));
+  if (out_f32)
+    ba::attn_fwd_kernel<D, WAVES, BLK, SPARSE, true><<<grid, WAVES * 64, 0, s>>>(p);
+  else
+    ba::attn_fwd_kernel<D, WAVES, BLK, SPARSE, false><<<grid, WAVES * 64, 0, s>>>(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ba_att_num_blocks(int32_t N, int32_t block) {
+  if (N < 1 || block < 1) return -1;
+  return num_blocks(N, block);
+}
+
+int32_t ba_att_keep_count(int32_t n_blocks, double sparsity) {
+  if (n_blocks < 1 || !(sparsity >= 0.0 && sparsity < 1.0)) return -1;
+  const long long drop = (long long)floor(sparsity * (double)n_blocks + 1e-9);
+  long long keep = (long long)n_blocks - drop;
+  if (keep < 1) keep = 1;
+  if (keep > n_blocks) keep = n_blocks;
+  return (int32_t)keep;
+}
+
+size_t ba_att_select_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block) {
+  if (check_shape(B, H, N, D) != BA_OK || block < 1) return 0;
+  const size_t n = (size_t)num_blocks(N, block);
+  return 2 * (size_t)B * H * n * 3 * D * sizeof(float);
+}
+
+int ba_att_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                  double sparsity, const void* q, const void* k, uint8_t* block_mask,
+                  int32_t* block_idx, int32_t* block_cnt, float* score, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  ba_status st = check_shape(B, H, N, D);
+  if (st != BA_OK) return st;
+  if (!q || !k || !block_mask || !block_idx || !block_cnt) return BA_ERR_INVALID_ARG;
+  if (!(sparsity >= 0.0 && sparsity < 1.0)) return BA_ERR_INVALID_ARG;
+  if (block != 64 && block != 128) return BA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(block_idx, 4) || !aligned(block_cnt, 4) ||
+      (score && !aligned(score, 4)))
+    return BA_ERR_INVALID_ARG;
+  const int n = num_blocks(N, block);
+  if (n > kMaxSelectBlocks) return BA_ERR_UNSUPPORTED;
+  const size_t need = ba_att_select_workspace_bytes(B, H, N, D, block);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return BA_ERR_WORKSPACE;
+  const int keep = ba_att_keep_count(n, sparsity);
+  const int BH = B * H;
+  const float sc = resolve_scale(scale, D);
+  float* aq = static_cast<float*>(workspace);
+  float* ak = aq + (size_t)BH * n * 3 * D;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  if (D == 128) {
+    launch_pool<128>(BH, N, n, block, sc, q16, k16, aq, ak, s);
+    launch_score<128>(BH, n, keep, aq, ak, block_mask, block_idx, block_cnt, score, s);
+  } else {
+    launch_pool<64>(BH, N, n, block, sc, q16, k16, aq, ak, s);
+    launch_score<64>(BH, n, keep, aq, ak, block_mask, block_idx, block_cnt, score, s);
+  }
+  return finish_launch();
+}
+
+int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* block_mask,
+                         int32_t max_keep, int32_t* block_idx, int32_t* block_cnt, void* stream) {
+  if (B < 1 || H < 1 || n_blocks < 1 || max_keep < 1) return BA_ERR_INVALID_ARG;
+  if (!block_mask || !block_idx || !block_cnt) return BA_ERR_INVALID_ARG;
+  if (!aligned(block_idx, 4) || !aligned(block_cnt, 4)) return BA_ERR_INVALID_ARG;
+  if (n_blocks > kMaxBlocksPerRow) return BA_ERR_UNSUPPORTED;
+  const long long rows = (long long)B * H * n_blocks;
+  if (rows * n_blocks >= (1ll << 31) || rows * max_keep >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  switch (ni_for(n_blocks)) {
+    case 1: ba::mask_to_index_kernel<1><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
+    case 2: ba::mask_to_index_kernel<2><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
+    case 4: ba::mask_to_index_kernel<4><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
+    case 8: ba::mask_to_index_kernel<8><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
+    default: ba::mask_to_index_kernel<16><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
+  }
+  return finish_launch();
+}
+
+int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                   const void* q, const void* k, const void* v, const int32_t* block_idx,
+                   const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
+                   float* lse, void* stream) {
+  ba_status st = check_shape(B, H, N, D);
+  if (st != BA_OK) return st;
+  if (!q || !k || !v || !block_idx || !block_cnt || !o) return BA_ERR_INVALID_ARG;
+  if (o_dtype != BA_BF16 && o_dtype != BA_F32) return BA_ERR_INVALID_ARG;
+  if (block != 64 && block != 128) return BA_ERR_UNSUPPORTED;
+  if (max_keep < 1) return BA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(block_idx, 4) || !aligned(block_cnt, 4) || (lse && !aligned(lse, 4)))
+    return BA_ERR_INVALID_ARG;
+  const int n = num_blocks(N, block);
+  if ((long long)B * H * n * max_keep >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  ba::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.idx = block_idx;
+  p.cnt = block_cnt;
+  p.o = o;
+  p.lse = lse;
+  p.N = N;
+  p.n_blocks = n;
+  p.n_qtiles = n;
+  p.total = B * H * n;
+  p.max_keep = max_keep;
+  p.scale_log2 = resolve_scale(scale, D) * 1.44269504088896340736f;
+  const bool f32 = o_dtype == BA_F32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 128) {
+    if (block == 64) launch_attn<128, 2, 64, true>(p, f32, s);
+    else launch_attn<128, 4, 128, true>(p, f32, s);
+  } else {
+    if (block == 64) launch_attn<64, 2, 64, true>(p, f32, s);
+    else launch_attn<64, 4, 128, true>(p, f32, s);
+  }
+  return finish_launch();
+}
+
+int ba_att_dense(int32_t B, int32_t H, int32_t N, int32_t D, float scale, const void* q,
+                 const void* k, const void* v, void* o, int32_t o_dtype, float* lse, void* stream) {
+  ba_status st = check_shape(B, H, N, D);
+  if (st != BA_OK) return st;
+  if (!q || !k || !v || !o) return BA_ERR_INVALID_ARG;
+  if (o_dtype != BA_BF16 && o_dtype != BA_F32) return BA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return BA_ERR_INVALID_ARG;
+  ba::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.N = N;
+  p.n_blocks = 0;
+  p.n_qtiles = (N + 127) / 128;
+  p.total = B * H * p.n_qtiles;
+  p.max_keep = 0;
+  p.scale_log2 = resolve_scale(scale, D) * 1.44269504088896340736f;
+  const bool f32 = o_dtype == BA_F32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 128) launch_attn<128, 4, 64, false>(p, f32, s);
+  else launch_attn<64, 4, 64, false>(p, f32, s);
+  return finish_launch();
+}
+
+const char* ba_att_status_string(int status) {
+  switch (status) {
+    case BA_OK: return "ok";
+    case BA_ERR_INVALID_ARG: return "invalid argument";
+    case BA_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case BA_ERR_WORKSPACE: return "workspace missing or too small";
+    case BA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

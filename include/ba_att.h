@@ -1,0 +1,140 @@
+/*
+ * ba_att.h -- C ABI of the MI355X (gfx950) Block Approximate Sparse Attention
+ * (BA-Att) operator.
+ *
+ * The operator is the one described in the pith.science review of
+ * "Efficient Long-Context Modeling in Diffusion Language Models via Block
+ * Approximate Sparse Attention" (arXiv 2605.19726), sections "The pith",
+ * "Core claim", "What carries the argument" and the abstract: attention for a
+ * bidirectional layer is computed in two passes,
+ *
+ *   1. selection -- pool Q and K per block (mean and diagonal variance),
+ *      score the compact block map with a correction built from the diagonal
+ *      QK variances, and norm-sort every query-block row to keep a fixed
+ *      number of key blocks (ba_att_select);
+ *   2. attention -- exact softmax attention of every query restricted to the
+ *      tokens of the kept key blocks (ba_att_forward).
+ *
+ * ba_att_dense is the full-attention comparator the speedup is quoted
+ * against (same review, "If this is right": acceleration over
+ * FlashAttention).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are contiguous, row-major [B, H, N, D] (D fastest); Q, K, V are
+ *    bf16 (raw 16-bit patterns), O is bf16 or fp32, LSE is fp32 [B, H, N].
+ *  - Blocks: n = ceil(N / block); block I holds tokens
+ *    [I*block, min((I+1)*block, N)); the last block may be partial.
+ *  - Block masks are uint8 [B, H, n, n] (row = query block, column = key
+ *    block, 1 = kept).  Block index lists are int32 [B, H, n, max_keep]
+ *    (kept key-block indices of each row, ascending) with int32 counts
+ *    [B, H, n].
+ *  - scale <= 0 selects the default softmax scale 1/sqrt(D).
+ *  - Supported: D in {64, 128}; block in {64, 128}; 1 <= N <= 2^20;
+ *    B*H*N*D < 2^31 elements.
+ *  - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *    16-byte aligned (the mask, idx and cnt buffers 4-byte aligned), owned by
+ *    the caller.  The library allocates nothing, keeps no state between
+ *    calls and never synchronises the host: work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the null stream) and completes asynchronously.
+ *  - Errors: every argument is checked on the host before anything is
+ *    launched; a failed check returns a nonzero ba_status and enqueues
+ *    nothing.  After the launches hipGetLastError() is checked and a launch
+ *    failure returns BA_ERR_HIP.  Faults during execution surface at the
+ *    caller's next synchronisation.
+ */
+#ifndef BA_ATT_H
+#define BA_ATT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BA_OK = 0,
+  BA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, sparsity outside [0,1), misalignment */
+  BA_ERR_UNSUPPORTED = 2, /* D or block outside the supported set, sizes too large */
+  BA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ba_att_select_workspace_bytes */
+  BA_ERR_HIP = 4          /* a HIP launch failed */
+} ba_status;
+
+typedef enum { BA_BF16 = 0, BA_F32 = 1 } ba_dtype;
+
+/* Number of blocks n = ceil(N / block) (block partition of the review's
+ * "The pith": the attention space is downsampled block-wise).  Returns -1
+ * when N < 1 or block < 1. */
+int32_t ba_att_num_blocks(int32_t N, int32_t block);
+
+/* Kept key blocks per query-block row at a block-sparsity ratio (review,
+ * "Core claim": half the blocks are dropped at 50% sparsity).  Fixed count
+ * keep = n - floor(sparsity*n + 1e-9), clamped to [1, n].  Returns -1 when
+ * n_blocks < 1 or sparsity is outside [0, 1). */
+int32_t ba_att_keep_count(int32_t n_blocks, double sparsity);
+
+/* Bytes of device workspace ba_att_select needs: the pooled block statistics
+ * of Q and K, 2 * B*H*n * 3*D fp32.  Returns 0 for invalid sizes. */
+size_t ba_att_select_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block);
+
+/* Selection pass (review, "What carries the argument": block-wise
+ * pre-downsampling, norm sorting and the diagonal-variance correction).
+ *
+ * For every (b, h) and block, means m and population variances v of Q and
+ * K over the block's valid tokens; then the corrected compact score
+ *   S[I,J] = scale*<mq_I, mk_J>
+ *          + scale^2/2 * sum_c (vq_Ic*vk_Jc + vq_Ic*mk_Jc^2 + mq_Ic^2*vk_Jc)
+ * and, per query-block row, the keep = ba_att_keep_count(n, sparsity) key
+ * blocks of largest S (ties: lower J first).
+ *
+ *   q, k        bf16 [B,H,N,D]                                     (in)
+ *   block_mask  uint8 [B,H,n,n], 1 = kept                          (out)
+ *   block_idx   int32 [B,H,n,keep], kept J ascending               (out)
+ *   block_cnt   int32 [B,H,n], all equal to keep                   (out)
+ *   score       fp32 [B,H,n,n] (the map S), or NULL to skip        (out)
+ *   workspace   >= ba_att_select_workspace_bytes(...) bytes        (scratch)
+ * Supported here: n <= 512 (otherwise BA_ERR_UNSUPPORTED). */
+int ba_att_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                  double sparsity, const void* q, const void* k, uint8_t* block_mask,
+                  int32_t* block_idx, int32_t* block_cnt, float* score, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Compacts a block mask into index lists, so a caller's own mask can drive
+ * ba_att_forward.  Per row: block_cnt = number of ones; block_idx holds the
+ * ascending indices of the first min(cnt, max_keep) ones (a row with more
+ * than max_keep ones is truncated, detectable as cnt > max_keep).
+ *   block_mask uint8 [B,H,n,n] (in); block_idx int32 [B,H,n,max_keep],
+ *   block_cnt int32 [B,H,n] (out).  Supported: n <= 1024. */
+int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* block_mask,
+                         int32_t max_keep, int32_t* block_idx, int32_t* block_cnt, void* stream);
+
+/* Block-sparse attention pass (review, "The pith": attention only over the
+ * selected blocks).  For every valid query s of block I, exact softmax over
+ * the tokens t < N of the key blocks block_idx[b,h,I,0:cnt) with
+ * cnt = min(block_cnt[b,h,I], max_keep):
+ *   LSE_s = ln sum_t exp(scale*<q_s,k_t>),  O_s = sum_t exp(scale*<q_s,k_t> - LSE_s) v_t.
+ * Entries outside [0, n) are skipped; entries must be distinct (a repeated
+ * entry is counted twice).  A row with no valid entry gives O = 0 and
+ * LSE = -inf.
+ *   q, k, v  bf16 [B,H,N,D] (in); block_idx/block_cnt as above (in);
+ *   o        [B,H,N,D] of o_dtype (BA_BF16 or BA_F32) (out);
+ *   lse      fp32 [B,H,N] natural log including the scale, or NULL (out). */
+int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                   const void* q, const void* k, const void* v, const int32_t* block_idx,
+                   const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
+                   float* lse, void* stream);
+
+/* Dense bidirectional attention softmax(scale*Q K^T) V with its LSE; the
+ * comparator of the sparse pass.  Arguments as in ba_att_forward. */
+int ba_att_dense(int32_t B, int32_t H, int32_t N, int32_t D, float scale, const void* q,
+                 const void* k, const void* v, void* o, int32_t o_dtype, float* lse, void* stream);
+
+/* Static description of a status code. */
+const char* ba_att_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BA_ATT_H */

@@ -1,0 +1,148 @@
+"""C-ABI contract checks that run without a GPU: the library loads, exports
+every symbol the header declares, its host-only helpers agree with the
+oracle's integer rules, and invalid arguments are rejected before anything is
+launched (these calls never reach the HIP runtime)."""
+
+import os
+import re
+
+import pytest
+
+from oracle import ba_att_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ba_att.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_attention_ba_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_ba_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ba_att_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("ba_att_select", "ba_att_forward", "ba_att_dense", "ba_att_mask_to_index",
+                 "ba_att_num_blocks", "ba_att_keep_count", "ba_att_select_workspace_bytes",
+                 "ba_att_status_string"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from block_sparse_attention_ba_amd import _lib
+    bound = {name for name, _, _ in _lib.SIGNATURES}
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in bound, f"{name} has no binding signature"
+
+
+def test_num_blocks_matches_oracle(lib):
+    for N in (1, 63, 64, 65, 1000, 1024, 8192, 16384, 32760, 32768):
+        for b in (64, 128):
+            assert lib.ba_att_num_blocks(N, b) == orc.num_blocks(N, b)
+    assert lib.ba_att_num_blocks(0, 64) == -1
+
+
+def test_keep_count_matches_oracle_bit_exactly(lib):
+    sps = [0.0, 0.1, 0.25, 0.29, 1 / 3, 0.3, 0.5, 0.7, 0.75, 0.9, 0.99, 0.999]
+    for n in list(range(1, 80)) + [128, 255, 256, 512, 1024]:
+        for sp in sps:
+            assert lib.ba_att_keep_count(n, sp) == orc.keep_count(n, sp), (n, sp)
+    assert lib.ba_att_keep_count(16, 1.0) == -1
+    assert lib.ba_att_keep_count(16, -0.5) == -1
+    assert lib.ba_att_keep_count(0, 0.5) == -1
+
+
+def test_workspace_bytes(lib):
+    assert lib.ba_att_select_workspace_bytes(1, 32, 8192, 128, 64) == 2 * 32 * 128 * 384 * 4
+    assert lib.ba_att_select_workspace_bytes(1, 40, 32760, 128, 128) == 2 * 40 * 256 * 384 * 4
+    assert lib.ba_att_select_workspace_bytes(1, 1, 1024, 96, 64) == 0
+
+
+def test_status_strings(lib):
+    for code, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape or size"),
+                       (3, b"workspace missing or too small"), (4, b"HIP launch failed")):
+        assert lib.ba_att_status_string(code) == text
+
+
+FAKE = 0x10000  # an aligned non-null value: every call below fails validation first
+
+
+def test_select_rejects_before_launch(lib):
+    ok = dict(B=1, H=1, N=1024, D=64, block=64, scale=0.0, sp=0.5)
+
+    def call(**kw):
+        a = dict(ok, q=FAKE, k=FAKE, mask=FAKE, idx=FAKE, cnt=FAKE, score=None, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.ba_att_select(a["B"], a["H"], a["N"], a["D"], a["block"], a["scale"], a["sp"],
+                                 a["q"], a["k"], a["mask"], a["idx"], a["cnt"], a["score"], a["ws"],
+                                 a["wsb"], None)
+
+    assert call(q=None) == 1
+    assert call(idx=None) == 1
+    assert call(sp=1.0) == 1 and call(sp=-0.1) == 1 and call(sp=float("nan")) == 1
+    assert call(N=0) == 1 and call(B=0) == 1
+    assert call(D=96) == 2
+    assert call(block=32) == 2
+    assert call(N=513 * 64) == 2             # more than 512 blocks per row
+    assert call(q=FAKE + 2) == 1             # misaligned
+    assert call(ws=None) == 3
+    assert call(wsb=16) == 3
+
+
+def test_forward_and_dense_reject_before_launch(lib):
+    def fwd(**kw):
+        a = dict(B=1, H=1, N=1024, D=128, block=64, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE,
+                 mk=8, o=FAKE, od=1, lse=None)
+        a.update(kw)
+        return lib.ba_att_forward(a["B"], a["H"], a["N"], a["D"], a["block"], 0.0, a["q"], a["k"],
+                                  a["v"], a["idx"], a["cnt"], a["mk"], a["o"], a["od"], a["lse"], None)
+
+    assert fwd(v=None) == 1 and fwd(o=None) == 1 and fwd(cnt=None) == 1
+    assert fwd(od=7) == 1
+    assert fwd(mk=0) == 1
+    assert fwd(D=80) == 2 and fwd(block=256) == 2
+    assert fwd(o=FAKE + 8) == 1
+    assert fwd(lse=FAKE + 2) == 1
+
+    def dense(**kw):
+        a = dict(B=1, H=1, N=1024, D=128, q=FAKE, k=FAKE, v=FAKE, o=FAKE, od=0, lse=None)
+        a.update(kw)
+        return lib.ba_att_dense(a["B"], a["H"], a["N"], a["D"], 0.0, a["q"], a["k"], a["v"],
+                                a["o"], a["od"], a["lse"], None)
+
+    assert dense(q=None) == 1 and dense(D=32) == 2 and dense(N=-1) == 1 and dense(od=2) == 1
+    assert dense(N=(1 << 20) + 1) == 2
+    assert dense(B=1 << 16, H=1 << 8) == 2  # too many elements
+
+
+def test_mask_to_index_rejects_before_launch(lib):
+    def m2i(**kw):
+        a = dict(B=1, H=1, n=16, mask=FAKE, mk=16, idx=FAKE, cnt=FAKE)
+        a.update(kw)
+        return lib.ba_att_mask_to_index(a["B"], a["H"], a["n"], a["mask"], a["mk"], a["idx"],
+                                        a["cnt"], None)
+
+    assert m2i(mask=None) == 1 and m2i(mk=0) == 1 and m2i(n=0) == 1
+    assert m2i(n=1025) == 2
+    assert m2i(idx=FAKE + 1) == 1
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    from block_sparse_attention_ba_amd import _lib
+    saved = _lib._lib
+    try:
+        _lib._lib = None
+        with pytest.raises(ImportError):
+            _lib.load(str(tmp_path / "missing.so"))
+    finally:
+        _lib._lib = saved

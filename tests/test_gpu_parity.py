@@ -1,0 +1,252 @@
+"""HIP path vs the fp64 oracle on seeded inputs small enough for the oracle
+to finish in seconds, spanning several tiles and ragged tails, plus the edge
+cases of the operator.  Everything runs through the C ABI.
+
+Bars: masks bit-exact except rows whose oracle cut margin is below 1e-4
+relative (counted); O max abs error <= 1e-2 and LSE within 1e-3 (fp32
+output); index work bit-exact."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_ba_amd import workloads as wl
+from oracle import ba_att_oracle as orc
+from tests.helpers import LSE_TOL, O_TOL, compare_masks, max_abs, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rand_bits(shape, seed, scale=1.0, mean=0.0):
+    rng = np.random.default_rng(seed)
+    x = (mean + scale * rng.standard_normal(shape)).astype(np.float32)
+    return wl.f32_to_bf16_bits(x)
+
+
+def clustered_bits(B, H, N, D, seed):
+    """Block-structured inputs (means shared by runs of tokens) so that
+    scores have clear winners as well as ties-free cuts."""
+    rng = np.random.default_rng(seed)
+    mu = rng.standard_normal((B, H, 8, D)).astype(np.float32)
+    lab = rng.integers(0, 8, size=(B, H, (N + 31) // 32)).repeat(32, axis=-1)[..., :N]
+    base = np.take_along_axis(mu, lab[..., None].repeat(D, -1), axis=2)
+    q = base + 0.5 * rng.standard_normal((B, H, N, D)).astype(np.float32)
+    k = base + 0.5 * rng.standard_normal((B, H, N, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    return wl.f32_to_bf16_bits(q), wl.f32_to_bf16_bits(k), wl.f32_to_bf16_bits(v)
+
+
+SELECT_CASES = [
+    # (B, H, N, D, block, sparsity, kind)
+    (1, 1, 1024, 64, 64, 0.5, "normal"),
+    (1, 2, 1000, 64, 64, 0.5, "clustered"),     # ragged tail of 40 tokens
+    (2, 2, 2048, 128, 64, 0.75, "clustered"),
+    (1, 3, 2000, 128, 128, 0.5, "clustered"),   # tail of 80 tokens
+    (1, 2, 4096, 128, 128, 0.0, "normal"),
+    (1, 1, 200, 128, 128, 0.5, "normal"),       # 2 blocks, tail of 72
+    (1, 1, 50, 64, 64, 0.5, "normal"),          # a single partial block
+    (1, 2, 8192, 128, 64, 0.9, "clustered"),    # 128 blocks per row
+    (1, 1, 16384, 64, 64, 0.5, "normal"),       # 256 blocks per row
+    (1, 1, 20000, 128, 64, 0.5, "clustered"),   # 313 blocks: 5 elements per lane
+]
+
+
+def make_case(B, H, N, D, kind, seed):
+    if kind == "normal":
+        return (rand_bits((B, H, N, D), seed), rand_bits((B, H, N, D), seed + 1),
+                rand_bits((B, H, N, D), seed + 2))
+    return clustered_bits(B, H, N, D, seed)
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_select_matches_oracle(gpu_lib, case):
+    import torch
+    B, H, N, D, block, sp, kind = case
+    _log("select case", case)
+    q, k, _ = make_case(B, H, N, D, kind, seed=N + D + block)
+    ref = orc.select_oracle(q, k, block, sp)
+    n, keep = ref["n"], ref["keep"]
+    ws = torch.empty(gpu_lib.select_workspace_bytes(B, H, N, D, block), dtype=torch.uint8, device="cuda")
+    mask, idx, cnt, score = gpu_lib.select(to_dev(q), to_dev(k), block, sp, return_score=True, workspace=ws)
+    torch.cuda.synchronize()
+    mask, idx, cnt, score = (t.cpu().numpy() for t in (mask, idx, cnt, score))
+
+    # pooled statistics in the caller's workspace: [aq | ak], 3D fp32 per block
+    aw = ws.view(torch.float32).cpu().numpy().astype(np.float64)
+    aq = aw[: B * H * n * 3 * D].reshape(B, H, n, 3 * D)
+    ak = aw[B * H * n * 3 * D:].reshape(B, H, n, 3 * D)
+    sc = 1 / math.sqrt(D)
+    assert np.allclose(aq[..., :D], sc * ref["qm"], rtol=1e-5, atol=1e-6)
+    assert np.allclose(aq[..., D:2 * D], 0.5 * sc * sc * ref["qv"], rtol=1e-4, atol=1e-7)
+    assert np.allclose(ak[..., :D], ref["km"], rtol=1e-5, atol=1e-6)
+    assert np.allclose(ak[..., 2 * D:], ref["kv"], rtol=1e-4, atol=1e-6)
+
+    # score map: fp32 dot of 3D terms; bound by a few ulps of the sum of |terms|
+    S = ref["S"]
+    mag = np.einsum("bhic,bhjc->bhij", np.abs(aq), np.abs(ak))
+    err = np.abs(score - S)
+    assert np.all(err <= 4e-5 * mag + 1e-7), float((err / (mag + 1e-30)).max())
+
+    assert np.all(cnt == keep)
+    res = compare_masks(mask, S, ref["mask"], keep)
+    _log("  rows", res["rows"], "exact", res["exact"], "near-tie rows", res["near_tie_rows"],
+         "near-tie mismatches", res["near_tie_mismatch"], "bad", len(res["bad"]))
+    assert not res["bad"], res["bad"][:10]
+    # idx is the ascending list of the mask's ones
+    for r, row in enumerate(mask.reshape(-1, n)):
+        assert np.array_equal(idx.reshape(-1, keep)[r], np.flatnonzero(row))
+
+
+ATTN_CASES = [
+    # (B, H, N, D, block, sparsity)
+    (1, 1, 1024, 64, 64, 0.5),
+    (1, 2, 1000, 64, 64, 0.5),
+    (1, 2, 1100, 128, 64, 0.5),
+    (2, 1, 1500, 128, 128, 0.5),
+    (1, 2, 2048, 128, 128, 0.75),
+    (1, 1, 200, 128, 128, 0.0),
+    (1, 1, 50, 64, 64, 0.0),
+    (1, 2, 1000, 64, 128, 0.5),
+    (1, 1, 4096, 128, 64, 0.9),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_forward_with_oracle_mask(gpu_lib, case):
+    import torch
+    B, H, N, D, block, sp = case
+    _log("forward case", case)
+    q, k, v = make_case(B, H, N, D, "clustered", seed=3 * N + D)
+    ref = orc.select_oracle(q, k, block, sp)
+    idx = torch.from_numpy(ref["idx"]).cuda()
+    cnt = torch.from_numpy(ref["cnt"]).cuda()
+    o, lse = gpu_lib.forward(to_dev(q), to_dev(k), to_dev(v), idx, cnt, block, out_dtype=torch.float32)
+    o16, lse16 = gpu_lib.forward(to_dev(q), to_dev(k), to_dev(v), idx, cnt, block, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    o16 = o16.float().cpu().numpy()
+    att = orc.attention_oracle(q, k, v, ref["mask"], block)
+    for (bi, hi), (Oo, Lo) in att.items():
+        eo, el = max_abs(o[bi, hi], Oo), max_abs(lse[bi, hi], Lo)
+        _log(f"  head {bi},{hi}: max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+        assert eo <= O_TOL and el <= LSE_TOL
+    # bf16 output is the fp32 result rounded once
+    assert np.all(np.abs(o16 - o) <= np.abs(o) * 2.0 ** -8 + 1e-6)
+    assert np.array_equal(lse16.cpu().numpy(), lse)
+
+
+@pytest.mark.parametrize("case", [(1, 1, 1024, 64), (1, 2, 1000, 128), (2, 1, 777, 64), (1, 1, 64, 128)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_dense_matches_oracle(gpu_lib, case):
+    import torch
+    B, H, N, D = case
+    _log("dense case", case)
+    q, k, v = (rand_bits((B, H, N, D), 10 + i, scale=1.5) for i in range(3))
+    o, lse = gpu_lib.dense(to_dev(q), to_dev(k), to_dev(v), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    sc = 1 / math.sqrt(D)
+    for bi in range(B):
+        for hi in range(H):
+            Oo, Lo = orc.dense_attention(orc.bf16_bits_to_f64(q[bi, hi]), orc.bf16_bits_to_f64(k[bi, hi]),
+                                         orc.bf16_bits_to_f64(v[bi, hi]), sc)
+            assert max_abs(o[bi, hi], Oo) <= O_TOL
+            assert max_abs(lse[bi, hi], Lo) <= LSE_TOL
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_zero_sparsity_equals_dense_bitwise(gpu_lib, block):
+    import torch
+    B, H, N, D = 1, 2, 1000, 128
+    q, k, v = (to_dev(rand_bits((B, H, N, D), 20 + i)) for i in range(3))
+    mask, idx, cnt = gpu_lib.select(q, k, block, 0.0)
+    o_s, l_s = gpu_lib.forward(q, k, v, idx, cnt, block)
+    o_d, l_d = gpu_lib.dense(q, k, v)
+    torch.cuda.synchronize()
+    assert bool((mask == 1).all())
+    assert torch.equal(l_s, l_d)
+    assert torch.equal(o_s, o_d)
+
+
+def test_mask_to_index_bit_exact_and_edge_rows(gpu_lib):
+    import torch
+    rng = np.random.default_rng(0)
+    for n in (1, 5, 64, 65, 200, 512, 1024):
+        m = (rng.random((2, 1, n, n)) < 0.4).astype(np.uint8)
+        m[0, 0, 0] = 0          # an empty row
+        m[0, 0, -1] = 1         # a full row
+        max_keep = n
+        idx, cnt = gpu_lib.mask_to_index(torch.from_numpy(m).cuda(), max_keep)
+        torch.cuda.synchronize()
+        idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+        for r, row in enumerate(m.reshape(-1, n)):
+            ones = np.flatnonzero(row)
+            assert cnt.reshape(-1)[r] == ones.size
+            assert np.array_equal(idx.reshape(-1, max_keep)[r][: ones.size], ones)
+    # truncation: cnt reports the full count, idx holds the lowest max_keep
+    m = np.ones((1, 1, 8, 8), np.uint8)
+    idx, cnt = gpu_lib.mask_to_index(torch.from_numpy(m).cuda(), 3)
+    torch.cuda.synchronize()
+    assert np.all(cnt.cpu().numpy() == 8) and np.all(idx.cpu().numpy() == np.arange(3))
+
+
+def test_empty_rows_and_invalid_entries(gpu_lib):
+    import torch
+    B, H, N, D, block = 1, 1, 700, 64, 64
+    q, k, v = make_case(B, H, N, D, "clustered", seed=99)
+    n = orc.num_blocks(N, block)
+    rng = np.random.default_rng(1)
+    mask = (rng.random((B, H, n, n)) < 0.5).astype(np.uint8)
+    mask[0, 0, 3] = 0  # empty row -> O = 0, LSE = -inf
+    idx, cnt = gpu_lib.mask_to_index(torch.from_numpy(mask).cuda())
+    # invalid entries are skipped: append an out-of-range index to row 5
+    idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
+    c5 = cnt_np[0, 0, 5]
+    if c5 < n:
+        idx_np[0, 0, 5, c5] = n + 7
+        cnt_np[0, 0, 5] = c5 + 1
+    o, lse = gpu_lib.forward(to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(idx_np).cuda(),
+                             torch.from_numpy(cnt_np).cuda(), block)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy()[0, 0], lse.cpu().numpy()[0, 0]
+    Oo, Lo = orc.attention_oracle(q, k, v, mask, block)[(0, 0)]
+    assert np.all(o[3 * 64:4 * 64] == 0) and np.all(np.isneginf(lse[3 * 64:4 * 64]))
+    assert max_abs(o, Oo) <= O_TOL and max_abs(lse, Lo) <= LSE_TOL
+
+
+def test_runs_are_deterministic(gpu_lib):
+    import torch
+    q, k, v = (to_dev(x) for x in make_case(1, 4, 4096, 128, "clustered", seed=5))
+    outs = []
+    for _ in range(2):
+        mask, idx, cnt, score = gpu_lib.select(q, k, 64, 0.5, return_score=True)
+        o, lse = gpu_lib.forward(q, k, v, idx, cnt, 64, out_dtype=torch.bfloat16)
+        od, ld = gpu_lib.dense(q, k, v, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (mask, idx, cnt, score, o, lse, od, ld)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_custom_scale_and_end_to_end_tiny(gpu_lib):
+    """The tiny workload end to end (select on the GPU, then forward with the
+    GPU's own mask) against the oracle, with a non-default softmax scale."""
+    import torch
+    x = wl.make_inputs("tiny")
+    scale = 0.2
+    q, k, v = (to_dev(x[t]) for t in ("q", "k", "v"))
+    mask, idx, cnt = gpu_lib.select(q, k, 64, 0.5, scale=scale)
+    o, lse = gpu_lib.forward(q, k, v, idx, cnt, 64, scale=scale)
+    torch.cuda.synchronize()
+    ref = orc.select_oracle(x["q"], x["k"], 64, 0.5, scale=scale)
+    res = compare_masks(mask.cpu().numpy(), ref["S"], ref["mask"], ref["keep"])
+    assert not res["bad"]
+    Oo, Lo = orc.attention_oracle(x["q"], x["k"], x["v"], mask.cpu().numpy(), 64, scale=scale)[(0, 0)]
+    assert max_abs(o.cpu().numpy()[0, 0], Oo) <= O_TOL
+    assert max_abs(lse.cpu().numpy()[0, 0], Lo) <= LSE_TOL
