@@ -1,0 +1,290 @@
+"""Benchmark of the BA-Att hot path on one MI355X.
+
+A step is one pass of the whole hot path on one batch of synthetic input:
+the selection pass (pool + corrected score + norm sort) followed by the
+block-sparse attention pass, at the workload's sparsity.  The default
+workload is the LLaDA-8B-shaped layer (B1 H32 N8192 D128, block 64, 50%
+sparsity, Q/K/V ~ N(0,1) with 2% planted salient keys).
+
+Prints ONE JSON line: dense-equivalent attention TFLOP/s of the step
+(4*B*H*N^2*D per step / step time), the speedup over this library's own
+dense kernel, a roofline object for the dominant kernel (the sparse
+attention kernel, bf16 MFMA), one for the selection pass (HBM), and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["block_sparse_attention_ba_amd/csrc/attention.hpp",
+                  "block_sparse_attention_ba_amd/csrc/select.hpp",
+                  "block_sparse_attention_ba_amd/csrc/common.hpp",
+                  "block_sparse_attention_ba_amd/csrc/ba_att.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llada8b")
+    ap.add_argument("--sparsity", type=float, default=None)
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline")
+    ap.add_argument("--skip-dense", action="store_true", help="omit the dense comparator")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def kept_tile_flops(mask, N: int, D: int, block: int) -> float:
+    """4*D*sum over kept (I, J) of |I|*|J| (true sizes of a partial tail)."""
+    import numpy as np
+    n = mask.shape[-1]
+    sizes = np.array([min(block, N - i * block) for i in range(n)], dtype=np.float64)
+    m = mask.reshape(-1, n, n).astype(np.float64)
+    return float(4.0 * D * np.einsum("bij,i,j->", m, sizes, sizes))
+
+
+def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
+    """The fp64 oracle as it stands, timed on this host: selection plus
+    block-sparse attention head by head until the time budget is used."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import ba_att_oracle as orc
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        for bh in heads:
+            sel = orc.select_oracle(x["q"], x["k"], w.block, sp, heads=[bh])
+            orc.attention_oracle(x["q"], x["k"], x["v"], sel["mask"], w.block, heads=[bh])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.N * w.N * w.D * done
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of the same workload (selection + "
+                      f"block-sparse attention, fp64 numpy), {dt:.1f} s on {model or 'host CPU'}; "
+                      "dense-equivalent FLOPs of the sampled heads / wall time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the operator has no "
+              "multi-GPU path in this build; every head is independent, so a multi-GPU run "
+              "would shard (batch, head) pairs with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_ba_amd import _lib, api, workloads
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_ba_amd import build
+        build.build()
+    api.load()
+
+    w = workloads.WORKLOADS[args.workload]
+    sp = args.sparsity if args.sparsity is not None else (0.5 if 0.5 in w.sparsities else w.sparsities[0])
+    x = workloads.make_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
+    B, H, N, D, blk = w.B, w.H, w.N, w.D, w.block
+    n = api.num_blocks(N, blk)
+    keep = api.keep_count(n, sp)
+    odt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    ws = torch.empty(api.select_workspace_bytes(B, H, N, D, blk), dtype=torch.uint8, device=dev)
+    mask = torch.empty((B, H, n, n), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, N, D), dtype=odt, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    code = 0 if odt == torch.bfloat16 else 1
+
+    def select():
+        st = lib.ba_att_select(B, H, N, D, blk, 0.0, sp, q.data_ptr(), k.data_ptr(), mask.data_ptr(),
+                               idx.data_ptr(), cnt.data_ptr(), None, ws.data_ptr(), ws.numel(), sptr)
+        if st:
+            raise RuntimeError(lib.ba_att_status_string(st).decode())
+
+    def sparse():
+        st = lib.ba_att_forward(B, H, N, D, blk, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                idx.data_ptr(), cnt.data_ptr(), keep, o.data_ptr(), code,
+                                lse.data_ptr(), sptr)
+        if st:
+            raise RuntimeError(lib.ba_att_status_string(st).decode())
+
+    def dense():
+        st = lib.ba_att_dense(B, H, N, D, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              o.data_ptr(), code, lse.data_ptr(), sptr)
+        if st:
+            raise RuntimeError(lib.ba_att_status_string(st).decode())
+
+    print(f"[bench] workload {w.name}: B{B} H{H} N{N} D{D} block {blk} sparsity {sp} keep {keep}/{n}",
+          file=sys.stderr, flush=True)
+
+    # ---- the timed hot path: K steps of select + sparse attention
+    for _ in range(args.warmup):
+        select()
+        sparse()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        select()
+        e1.record(stream)
+        sparse()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sel_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    spa_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    step_ms = wall * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {step_ms:.4f} ms/step (select {sel_ms:.4f} ms, "
+          f"sparse attention {spa_ms:.4f} ms)", file=sys.stderr, flush=True)
+
+    mask_np = mask.cpu().numpy()
+    kept_flops = kept_tile_flops(mask_np, N, D, blk)
+    dense_flops = 4.0 * B * H * N * N * D
+
+    # ---- selection pass with the last-level caches flushed (honest HBM figure)
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    sel_flushed = []
+    for i in range(args.warmup + args.steps):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        select()
+        b.record(stream)
+        if i >= args.warmup:
+            sel_flushed.append((a, b))
+    torch.cuda.synchronize()
+    sel_flush_ms = float(np.median([a.elapsed_time(b) for a, b in sel_flushed]))
+    del flush
+    sel_bytes = 2.0 * B * H * N * D * 2 + B * H * n * n + 4.0 * B * H * n * keep + 4.0 * B * H * n
+
+    # ---- the dense comparator
+    dense_ms = None
+    if not args.skip_dense:
+        for _ in range(args.warmup):
+            dense()
+        torch.cuda.synchronize()
+        evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(5, args.steps // 2))]
+        for a, b in evd:
+            a.record(stream)
+            dense()
+            b.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in evd]))
+        print(f"[bench] dense {dense_ms:.4f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s)",
+              file=sys.stderr, flush=True)
+
+    # ---- HBM traffic from the committed counter runs, if they match these kernels
+    traffic = None
+    src_hash = kernel_source_hash()
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tc = json.load(f)
+        entry = tc.get("workloads", {}).get(f"{w.name}:{sp}:{args.out_dtype}")
+        if tc.get("kernel_source_hash") == src_hash and entry:
+            traffic = entry.get("attention_bytes_per_launch")
+            sel_traffic = entry.get("select_bytes_per_call")
+        else:
+            sel_traffic = None
+    except (OSError, ValueError):
+        sel_traffic = None
+
+    achieved = kept_flops / (spa_ms * 1e-3) / 1e12
+    value = dense_flops / (step_ms * 1e-3) / 1e12
+    sel_gbs = sel_bytes / (sel_flush_ms * 1e-3) / 1e9
+    result = {
+        "metric": "dense-equiv attention TFLOP/s + speedup vs own dense kernel @50% sparsity",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.description, "name": w.name, "B": B, "H": H, "N": N, "D": D,
+                   "block": blk, "sparsity": sp, "keep": keep, "n_blocks": n,
+                   "out_dtype": args.out_dtype, "parallelism": "single GPU"},
+        "speedup_vs_dense": round(dense_ms / step_ms, 4) if dense_ms else None,
+        "dense_ms": round(dense_ms, 5) if dense_ms else None,
+        "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
+        "select_ms": round(sel_ms, 5),
+        "sparse_attention_ms": round(spa_ms, 5),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel (sparse)",
+                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
+                     "work_per_launch": kept_flops},
+        "roofline_select": {"bound": "hbm", "kernel": "pool_stats_kernel + score_topk_kernel",
+                            "achieved": round(sel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,
+                            "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.skip_cpu:
+        print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x, w, sp, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

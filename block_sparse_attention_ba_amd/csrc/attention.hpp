@@ -6,24 +6,28 @@
 // its kept key blocks; the dense variant keeps every block and is the
 // comparator of the review's "If this is right" speedup claim.
 //
-// Design (per workgroup: one tile of 32*WAVES query rows of one (b, h)):
+// Design (one workgroup = one tile of 32*WAVES query rows of one (b, h)):
 //  * Each wave owns 32 query rows.  Scores are formed TRANSPOSED,
-//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 d from LDS,
-//    B = Q^T from registers (Q is loaded once).  In the 32x32 accumulator
-//    layout lane l then holds column l%32 -- a single query -- so the
-//    running max/sum of a query live in one lane pair (l, l^32) and need one
-//    cross-lane exchange per key chunk.
+//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 d from LDS,
+//    B = Q^T held in registers for the whole kernel).  In the 32x32
+//    accumulator layout lane l then holds column l%32 -- one query -- so the
+//    running max/sum of a query live in the lane pair (l, l^32).
 //  * The output is accumulated transposed too, O^T = V^T P^T: B = P^T comes
 //    straight from the score registers (fp32 -> bf16), A = V^T is read from a
-//    transposed V tile in LDS.  Every O register of a lane belongs to that
-//    lane's query, so the online-softmax rescale is lane-local.
-//  * Keys are processed in chunks of 64 (one block of 64, or half a block of
-//    128).  K (row-major, padded) and V^T (padded) are staged through LDS;
-//    the next chunk's global loads are in flight while the current chunk is
-//    computed.
+//    row-major V tile with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16).  Every O register of a lane belongs to that lane's
+//    query, so the online-softmax rescale is lane-local.
+//  * Keys are processed in chunks of 64.  K and V chunks are copied HBM/L2 ->
+//    LDS by direct-to-LDS loads (no register staging) into one K and one V
+//    buffer used in ping-pong: V(c) streams in while S^T(c) and the softmax
+//    run, K(c+1) streams in while O^T += V(c) P^T runs.  16-byte chunks of
+//    every row are XOR-swizzled so that both the row reads of K and the
+//    transposing reads of V are free of bank conflicts.
+//  * Online softmax in the log2 domain, fp32.  The accumulators of a wave are
+//    rescaled only in chunks where some query's running max grows (a
+//    wave-uniform branch), which becomes rare once the maxima settle.
 //  * The sparse variant walks the compacted block-index list of its query
 //    block; the dense variant walks all keys.  Keys >= N are masked to -inf.
-//  * Softmax runs in the log2 domain in fp32: p = exp2(s*scale*log2(e) - m).
 #pragma once
 
 #include "common.hpp"
@@ -47,41 +51,46 @@ struct AttnParams {
 };
 
 constexpr int kChunk = 64;  // keys per LDS chunk
+#ifndef BA_RESCALE_SLACK
+#define BA_RESCALE_SLACK 0.0f
+#endif
+// log2 headroom before the running max moves.  0 keeps the exact running max,
+// so the largest probability of a row is exactly 1 before bf16 rounding; a
+// positive slack skips more rescales but rounds that probability too.
+constexpr float kRescaleSlack = BA_RESCALE_SLACK;
 
-template <int D>
-struct AttnSmem {
-  static constexpr int KP = D + 8;        // K row pitch (bf16 elements)
-  static constexpr int VP = kChunk + 4;   // V^T row pitch (bf16 elements)
-  static constexpr int K_ELEMS = kChunk * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int BYTES = (K_ELEMS + V_ELEMS) * 2;
-};
+#define BA_LDS __attribute__((address_space(3)))
+#define BA_GLOBAL __attribute__((address_space(1)))
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte slot of logical chunk c in row r of a K tile / a V tile
+template <int CPR>
+__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r % CPR); }
+template <int CPR>
+__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r % (CPR / 2)) << 1); }
 
 template <int D, int WAVES, int BLK, bool SPARSE, bool OUT_F32>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
-  constexpr int NT = WAVES * 64;
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int ROWS = WAVES * 32;
   constexpr int KSTEPS = D / 16;          // MFMA k-steps of the score product
   constexpr int DT = D / 32;              // 32-wide d tiles of the output
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  constexpr int K_LOADS = (kChunk * CPR + NT - 1) / NT;
-  constexpr int V_ITEMS_TOTAL = (kChunk / 4) * CPR;  // items of 4 keys x 8 d
-  constexpr int V_ITEMS = (V_ITEMS_TOTAL + NT - 1) / NT;
+  constexpr int TILE_BYTES = kChunk * D * 2;
+  constexpr int DMA_PER_WAVE = (kChunk * CPR) / (64 * WAVES);  // 16-byte loads per lane per tile
   constexpr int SUBS = SPARSE ? BLK / kChunk : 1;  // chunks per listed block
-  using Sm = AttnSmem<D>;
   static_assert(!SPARSE || ROWS == BLK, "sparse tile must be one query block");
+  static_assert((kChunk * CPR) % (64 * WAVES) == 0, "tile must split evenly over the waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[Sm::K_ELEMS + Sm::V_ELEMS];
-  uint16_t* Ks = smem;
-  uint16_t* Vt = smem + Sm::K_ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TILE_BYTES];
+  uint8_t* Kbuf = smem;
+  uint8_t* Vbuf = smem + TILE_BYTES;
 
   const int logical = xcd_remap(blockIdx.x, p.total);
   if (logical < 0) return;
   const int bh = logical / p.n_qtiles;
   const int qt = logical - bh * p.n_qtiles;
   const int N = p.N;
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5;    // lane half
   const int lq = lane & 31;   // query column of this lane
 
@@ -112,6 +121,22 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
+  // ---- direct-to-LDS copy of one 64-key tile (rows clamped into [0, N))
+  auto dma_tile = [&](const uint16_t* src, uint8_t* dst, int k0, bool is_v) {
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      const int slot_lin = (j * WAVES + wave) * 64 + lane;
+      const int r = slot_lin / CPR;
+      const int s = slot_lin % CPR;
+      const int c = is_v ? (s ^ ((r % (CPR / 2)) << 1)) : (s ^ (r % CPR));
+      int row = k0 + r;
+      row = row < 0 ? 0 : (row >= N ? N - 1 : row);
+      const uint16_t* gp = src + (size_t)row * D + c * 8;
+      uint8_t* lp = dst + (j * WAVES + wave) * 64 * 16;  // wave-uniform base
+      __builtin_amdgcn_global_load_lds((BA_GLOBAL void*)gp, (BA_LDS void*)lp, 16, 0, 0);
+    }
+  };
+
   // ---- Q fragments (B operand of S^T = K Q^T), loaded once
   const int qrow = qt * ROWS + wave * 32 + lq;
   bf16x8 qf[KSTEPS];
@@ -122,67 +147,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
     qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
-  // ---- register staging of one chunk
-  u32x4 kreg[K_LOADS];
-  u32x4 vreg[V_ITEMS][4];
-  auto load_chunk = [&](int c) {
-    const int k0 = chunk_start(c);
-    const int valid = k0 < 0 ? 0 : min(kChunk, N - k0);
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int e = t + i * NT;
-      const int row = e / CPR, col = e % CPR;
-      kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if ((K_LOADS * NT == kChunk * CPR || e < kChunk * CPR) && row < valid)
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)(k0 + row) * D + col * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < V_ITEMS; ++i) {
-      const int e = t + i * NT;
-      const int c8 = e % CPR, kg = e / CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vreg[i][r] = u32x4{0u, 0u, 0u, 0u};
-        const int key = kg * 4 + r;
-        if ((V_ITEMS * NT == V_ITEMS_TOTAL || e < V_ITEMS_TOTAL) && key < valid)
-          vreg[i][r] = *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + key) * D + c8 * 8);
-      }
-    }
-    return valid;
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int e = t + i * NT;
-      if (K_LOADS * NT == kChunk * CPR || e < kChunk * CPR) {
-        const int row = e / CPR, col = e % CPR;
-        *reinterpret_cast<u32x4*>(Ks + row * Sm::KP + col * 8) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_ITEMS; ++i) {
-      const int e = t + i * NT;
-      if (V_ITEMS * NT == V_ITEMS_TOTAL || e < V_ITEMS_TOTAL) {
-        const int c8 = e % CPR, kg = e / CPR;
-        // transpose 4 keys x 8 d into 8 rows of V^T, 4 keys (8 bytes) each
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // d = 8*c8 + 2w (low halves) and 2w+1 (high halves)
-          const uint32_t a0 = vreg[i][0][w], a1 = vreg[i][1][w];
-          const uint32_t a2 = vreg[i][2][w], a3 = vreg[i][3][w];
-          u32x2 lo, hi;
-          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // (a0.lo, a1.lo)
-          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // (a0.hi, a1.hi)
-          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-          const int d0 = 8 * c8 + 2 * w;
-          *reinterpret_cast<u32x2*>(Vt + d0 * Sm::VP + kg * 4) = lo;
-          *reinterpret_cast<u32x2*>(Vt + (d0 + 1) * Sm::VP + kg * 4) = hi;
-        }
-      }
-    }
-  };
-
   // ---- running state of this lane's query
   f32x16 oacc[DT];
 #pragma unroll
@@ -191,13 +155,17 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
   float l_run = 0.f;
   const float sl2 = p.scale_log2;
 
-  int valid_next = 0;
-  if (n_chunks > 0) valid_next = load_chunk(0);
+  int k0_next = n_chunks > 0 ? chunk_start(0) : 0;
+  if (n_chunks > 0) dma_tile(Kh, Kbuf, k0_next, false);
+
   for (int c = 0; c < n_chunks; ++c) {
-    const int valid = valid_next;
-    store_chunk();
-    __syncthreads();
-    if (c + 1 < n_chunks) valid_next = load_chunk(c + 1);
+    const int k0 = k0_next;
+    const int valid = k0 < 0 ? 0 : min(kChunk, N - k0);
+    if (c + 1 < n_chunks) k0_next = chunk_start(c + 1);
+
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(c) landed
+    __syncthreads();  // K(c) visible to all waves; every wave is done with V(c-1)
+    dma_tile(Vh, Vbuf, k0, true);
 
     // S^T (64 keys x 32 queries) = K Q^T
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -205,7 +173,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + lq) * Sm::KP + ks * 16 + g * 8);
+        const int r = kt * 32 + lq;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            Kbuf + r * (D * 2) + k_slot<CPR>(r, ks * 2 + g) * 16);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
       }
     }
@@ -219,16 +189,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
           if (key >= valid) sacc[kt][r] = -__builtin_inff();
         }
     }
-    float mloc = sacc[0][0];
+    float mloc = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int r = 2; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[0][r], sacc[0][r + 1]));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kt][r]);
-    mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc * sl2);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32)) * sl2;
+    if (__any(mloc > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      if (m_new != -__builtin_inff()) {
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+        m_run = m_new;
+      }
+    }
+    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
     float psum = 0.f;
     bf16x8 pf[2][2];
@@ -247,28 +224,37 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
         pf[kt][s] = __builtin_bit_cast(bf16x8, w);
       }
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+    l_run += psum;
 
-    // O^T (D x 32 queries) += V^T P^T
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(c) landed
+    __syncthreads();  // V(c) visible; every wave is done with K(c)
+    if (c + 1 < n_chunks) dma_tile(Kh, Kbuf, k0_next, false);
+
+    // O^T (D x 32 queries) += V^T P^T; the A operand (32 d x 16 keys) comes
+    // from two transposing reads, keys base+4g+{0..3} and base+8+4g+{0..3}
+    const int grp = lane >> 4, li = lane & 15;
+    const int dl = 16 * (grp & 1) + 4 * (li & 3);  // d of this lane's 8-byte read
+    const int kr = li >> 2;                         // key row of this lane's read
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int kb = kt * 32 + s * 16 + 4 * g;
+        const int kbase = kt * 32 + s * 16 + 4 * (grp >> 1) + kr;
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
-          const uint16_t* vrow = Vt + (d * 32 + lq) * Sm::VP + kb;
-          u32x4 w;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kt][s], oacc[d], 0, 0, 0);
+          const int dd = d * 32 + dl;
+          const int r0 = kbase, r1 = kbase + 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (BA_LDS i16x4*)(Vbuf + r0 * (D * 2) + v_slot<CPR>(r0, dd >> 3) * 16 + (dd & 7) * 2));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (BA_LDS i16x4*)(Vbuf + r1 * (D * 2) + v_slot<CPR>(r1, dd >> 3) * 16 + (dd & 7) * 2));
+          const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
+                                                                 hi[0], hi[1], hi[2], hi[3]};
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pf[kt][s],
+                                                            oacc[d], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
   }
 
   // ---- epilogue
@@ -277,7 +263,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnParams p) {
   if (qrow < N) {
     if (p.lse != nullptr && g == 0) {
       p.lse[(size_t)bh * N + qrow] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
+          l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
     }
     if constexpr (OUT_F32) {
       float* Orow = reinterpret_cast<float*>(p.o) + head + (size_t)qrow * D;
