@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline")
     ap.add_argument("--skip-dense", action="store_true", help="omit the dense comparator")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for traffic counters)")
     return ap.parse_args()
 
 
@@ -168,6 +170,15 @@ def main():
 
     print(f"[bench] workload {w.name}: B{B} H{H} N{N} D{D} block {blk} sparsity {sp} keep {keep}/{n}",
           file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        # a plain copy of known size: reads 1 GiB and writes 1 GiB per dispatch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- the timed hot path: K steps of select + sparse attention
     for _ in range(args.warmup):

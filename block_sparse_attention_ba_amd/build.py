@@ -34,6 +34,8 @@ def compile_command(out: str) -> list[str]:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # inputs are finite: max/min need no NaN-quieting canonicalisation
+        "-fno-honor-nans",
         "-Wno-unused-command-line-argument",
         "-I", INCLUDE, "-I", CSRC,
         os.path.join(CSRC, "ba_att.hip"), "-o", out,

@@ -18,11 +18,13 @@
 //    (ds_read_b64_tr_b16).  Every O register of a lane belongs to that lane's
 //    query, so the online-softmax rescale is lane-local.
 //  * Keys are processed in chunks of 64.  K and V chunks are copied HBM/L2 ->
-//    LDS by direct-to-LDS loads (no register staging) into one K and one V
-//    buffer used in ping-pong: V(c) streams in while S^T(c) and the softmax
-//    run, K(c+1) streams in while O^T += V(c) P^T runs.  16-byte chunks of
-//    every row are XOR-swizzled so that both the row reads of K and the
-//    transposing reads of V are free of bank conflicts.
+//    LDS by direct-to-LDS buffer loads (no register staging; loads past the
+//    sequence end return zero) into one K and one V buffer used in
+//    ping-pong: V(c) streams in while S^T(c) and the softmax run, K(c+1)
+//    streams in while O^T += V(c) P^T runs.  16-byte chunks of every row are
+//    XOR-swizzled so that both the row reads of K and the transposing reads
+//    of V are free of bank conflicts.  MFMA operands are read from LDS one
+//    step ahead of their use.
 //  * Online softmax in the log2 domain, fp32.  The accumulators of a wave are
 //    rescaled only in chunks where some query's running max grows (a
 //    wave-uniform branch), which becomes rare once the maxima settle.
@@ -69,15 +71,43 @@ __device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r % CPR); }
 template <int CPR>
 __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r % (CPR / 2)) << 1); }
 
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3): loads past
+// the end return zero, which pads partial and skipped key chunks.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// max / sum of x over the lane pair (l, l^32) with one v_permlane32_swap
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Copy j of a 64-key tile: lane `lane` of wave `wave` fills LDS slot
+// (j*WAVES + wave)*64 + lane (16 bytes) from byte offset voff[j] of the tile.
+template <int DMA, int WAVES>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int wave,
+                                         const uint32_t* voff) {
+#pragma unroll
+  for (int j = 0; j < DMA; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (BA_LDS void*)(dst + (j * WAVES + wave) * 64 * 16),
+                                             16, voff[j], 0, 0, 0);
+}
+
 template <int D, int WAVES, int BLK, bool SPARSE, bool OUT_F32>
 __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int ROWS = WAVES * 32;
   constexpr int KSTEPS = D / 16;          // MFMA k-steps of the score product
   constexpr int DT = D / 32;              // 32-wide d tiles of the output
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  constexpr int TILE_BYTES = kChunk * D * 2;
-  constexpr int DMA_PER_WAVE = (kChunk * CPR) / (64 * WAVES);  // 16-byte loads per lane per tile
-  constexpr int SUBS = SPARSE ? BLK / kChunk : 1;  // chunks per listed block
+  constexpr int ROW_BYTES = D * 2;
+  constexpr int TILE_BYTES = kChunk * ROW_BYTES;
+  constexpr int DMA = (kChunk * CPR) / (64 * WAVES);  // 16-byte loads per lane per tile
+  constexpr int SUBS = SPARSE ? BLK / kChunk : 1;     // chunks per listed block
   static_assert(!SPARSE || ROWS == BLK, "sparse tile must be one query block");
   static_assert((kChunk * CPR) % (64 * WAVES) == 0, "tile must split evenly over the waves");
 
@@ -90,7 +120,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   const int bh = logical / p.n_qtiles;
   const int qt = logical - bh * p.n_qtiles;
   const int N = p.N;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;    // lane half
   const int lq = lane & 31;   // query column of this lane
 
@@ -121,20 +152,21 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // ---- direct-to-LDS copy of one 64-key tile (rows clamped into [0, N))
-  auto dma_tile = [&](const uint16_t* src, uint8_t* dst, int k0, bool is_v) {
+  // ---- direct-to-LDS tile copies: lane `lane` of wave `wave` fills LDS slot
+  // p = (j*WAVES + wave)*64 + lane (16 bytes) of copy j; the slot holds
+  // logical chunk c of row r under the tile's swizzle.  Byte offsets of the
+  // source chunks are loop-invariant.
+  uint32_t voff_k[DMA], voff_v[DMA];
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      const int slot_lin = (j * WAVES + wave) * 64 + lane;
-      const int r = slot_lin / CPR;
-      const int s = slot_lin % CPR;
-      const int c = is_v ? (s ^ ((r % (CPR / 2)) << 1)) : (s ^ (r % CPR));
-      int row = k0 + r;
-      row = row < 0 ? 0 : (row >= N ? N - 1 : row);
-      const uint16_t* gp = src + (size_t)row * D + c * 8;
-      uint8_t* lp = dst + (j * WAVES + wave) * 64 * 16;  // wave-uniform base
-      __builtin_amdgcn_global_load_lds((BA_GLOBAL void*)gp, (BA_LDS void*)lp, 16, 0, 0);
-    }
+  for (int j = 0; j < DMA; ++j) {
+    const int slot = (j * WAVES + wave) * 64 + lane;
+    const int r = slot / CPR, s = slot % CPR;
+    voff_k[j] = r * ROW_BYTES + (s ^ (r % CPR)) * 16;
+    voff_v[j] = r * ROW_BYTES + (s ^ ((r % (CPR / 2)) << 1)) * 16;
+  }
+  auto tile_rsrc = [&](const uint16_t* src, int k0) {
+    const int rows = k0 < 0 ? 0 : min(kChunk, N - k0);
+    return make_rsrc(src + (size_t)(k0 < 0 ? 0 : k0) * D, rows * ROW_BYTES);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), loaded once
@@ -147,6 +179,28 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
+  // ---- LDS operand reads
+  auto read_k = [&](int kt, int ks) -> bf16x8 {  // A of S^T: key kt*32+lq, d = 16ks+8g..+8
+    const int r = kt * 32 + lq;
+    return *reinterpret_cast<const bf16x8*>(Kbuf + r * ROW_BYTES + k_slot<CPR>(r, ks * 2 + g) * 16);
+  };
+  // A of O^T for d tile `dtile`, keys base+4g+{0..3} and base+8+4g+{0..3},
+  // base = 16*step: two transposing reads of the row-major V tile
+  const int grp = lane >> 4, li = lane & 15;
+  const int dl = 16 * (grp & 1) + 4 * (li & 3);  // d of this lane's 8-byte read
+  const int kr = 4 * (grp >> 1) + (li >> 2);      // key row of this lane's read within a step
+  auto read_v = [&](int step, int dtile) -> bf16x8 {
+    const int dd = dtile * 32 + dl;
+    const int r0 = step * 16 + kr, r1 = r0 + 8;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (BA_LDS i16x4*)(Vbuf + r0 * ROW_BYTES + v_slot<CPR>(r0, dd >> 3) * 16 + (dd & 7) * 2));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (BA_LDS i16x4*)(Vbuf + r1 * ROW_BYTES + v_slot<CPR>(r1, dd >> 3) * 16 + (dd & 7) * 2));
+    const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
+                                                           hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, a8);
+  };
+
   // ---- running state of this lane's query
   f32x16 oacc[DT];
 #pragma unroll
@@ -156,7 +210,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   const float sl2 = p.scale_log2;
 
   int k0_next = n_chunks > 0 ? chunk_start(0) : 0;
-  if (n_chunks > 0) dma_tile(Kh, Kbuf, k0_next, false);
+  if (n_chunks > 0) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
 
   for (int c = 0; c < n_chunks; ++c) {
     const int k0 = k0_next;
@@ -165,18 +219,23 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(c) landed
     __syncthreads();  // K(c) visible to all waves; every wave is done with V(c-1)
-    dma_tile(Vh, Vbuf, k0, true);
+    dma_tile<DMA, WAVES>(tile_rsrc(Vh, k0), Vbuf, wave, voff_v);
 
-    // S^T (64 keys x 32 queries) = K Q^T
+    // S^T (64 keys x 32 queries) = K Q^T, K operands read one k-step ahead
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    bf16x8 kcur[2] = {read_k(0, 0), read_k(1, 0)};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int r = kt * 32 + lq;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            Kbuf + r * (D * 2) + k_slot<CPR>(r, ks * 2 + g) * 16);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
+      bf16x8 knext[2];
+      if (ks + 1 < KSTEPS) {
+        knext[0] = read_k(0, ks + 1);
+        knext[1] = read_k(1, ks + 1);
+      }
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qf[ks], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[1], qf[ks], sacc[1], 0, 0, 0);
+      if (ks + 1 < KSTEPS) {
+        kcur[0] = knext[0];
+        kcur[1] = knext[1];
       }
     }
     // keys past the end of the sequence (or of a skipped entry)
@@ -194,11 +253,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     for (int r = 2; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[0][r], sacc[0][r + 1]));
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[1][r], sacc[1][r + 1]));
-    mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32)) * sl2;
+    mloc = pair_max(mloc) * sl2;
     if (__any(mloc > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mloc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
       if (m_new != -__builtin_inff()) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
         l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
@@ -208,7 +267,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
     float psum = 0.f;
-    bf16x8 pf[2][2];
+    bf16x8 pf[4];  // P^T operand of each 16-key step
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -221,44 +280,38 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
           psum += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
-        pf[kt][s] = __builtin_bit_cast(bf16x8, w);
+        pf[2 * kt + s] = __builtin_bit_cast(bf16x8, w);
       }
     }
     l_run += psum;
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(c) landed
     __syncthreads();  // V(c) visible; every wave is done with K(c)
-    if (c + 1 < n_chunks) dma_tile(Kh, Kbuf, k0_next, false);
+    if (c + 1 < n_chunks) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
 
-    // O^T (D x 32 queries) += V^T P^T; the A operand (32 d x 16 keys) comes
-    // from two transposing reads, keys base+4g+{0..3} and base+8+4g+{0..3}
-    const int grp = lane >> 4, li = lane & 15;
-    const int dl = 16 * (grp & 1) + 4 * (li & 3);  // d of this lane's 8-byte read
-    const int kr = li >> 2;                         // key row of this lane's read
+    // O^T (D x 32 queries) += V^T P^T, V operands read one step ahead
+    bf16x8 vcur[DT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int d = 0; d < DT; ++d) vcur[d] = read_v(0, d);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int kbase = kt * 32 + s * 16 + 4 * (grp >> 1) + kr;
+    for (int step = 0; step < 4; ++step) {
+      bf16x8 vnext[DT];
+      if (step + 1 < 4) {
 #pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          const int dd = d * 32 + dl;
-          const int r0 = kbase, r1 = kbase + 8;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (BA_LDS i16x4*)(Vbuf + r0 * (D * 2) + v_slot<CPR>(r0, dd >> 3) * 16 + (dd & 7) * 2));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (BA_LDS i16x4*)(Vbuf + r1 * (D * 2) + v_slot<CPR>(r1, dd >> 3) * 16 + (dd & 7) * 2));
-          const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
-                                                                 hi[0], hi[1], hi[2], hi[3]};
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pf[kt][s],
-                                                            oacc[d], 0, 0, 0);
-        }
+        for (int d = 0; d < DT; ++d) vnext[d] = read_v(step + 1, d);
+      }
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[d], pf[step], oacc[d], 0, 0, 0);
+      if (step + 1 < 4) {
+#pragma unroll
+        for (int d = 0; d < DT; ++d) vcur[d] = vnext[d];
       }
     }
   }
 
   // ---- epilogue
-  const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qrow < N) {
     if (p.lse != nullptr && g == 0) {
