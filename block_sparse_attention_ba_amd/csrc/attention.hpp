@@ -68,8 +68,14 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // 16-byte slot of logical chunk c in row r of a K tile / a V tile
 template <int CPR>
 __device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r % CPR); }
+// V: a transposing read serves 32 lanes = 4 key rows x 4 consecutive chunks
+// per cycle; XOR-ing 4*(row%4) (or, with 8 chunks per row, 4*((row/2)%2)
+// while consecutive rows fall in opposite bank halves) spreads them over all
+// 64 banks.
 template <int CPR>
-__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r % (CPR / 2)) << 1); }
+__device__ __forceinline__ int v_slot(int r, int c) {
+  return CPR >= 16 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
+}
 
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3): loads past
 // the end return zero, which pads partial and skipped key chunks.
@@ -161,8 +167,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   for (int j = 0; j < DMA; ++j) {
     const int slot = (j * WAVES + wave) * 64 + lane;
     const int r = slot / CPR, s = slot % CPR;
-    voff_k[j] = r * ROW_BYTES + (s ^ (r % CPR)) * 16;
-    voff_v[j] = r * ROW_BYTES + (s ^ ((r % (CPR / 2)) << 1)) * 16;
+    voff_k[j] = r * ROW_BYTES + k_slot<CPR>(r, s) * 16;
+    voff_v[j] = r * ROW_BYTES + v_slot<CPR>(r, s) * 16;
   }
   auto tile_rsrc = [&](const uint16_t* src, int k0) {
     const int rows = k0 < 0 ? 0 : min(kChunk, N - k0);
