@@ -207,11 +207,13 @@ def main():
     kept_flops = kept_tile_flops(mask_np, N, D, blk)
     dense_flops = 4.0 * B * H * N * N * D
 
-    # ---- selection pass with the last-level caches flushed (honest HBM figure)
-    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    # ---- selection pass with L2 and the MALL flushed by reading 1 GiB of
+    # unrelated data (a read leaves no dirty lines to write back)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     sel_flushed = []
     for i in range(args.warmup + args.steps):
-        flush.fill_(i & 0xFF)
+        torch.sum(flush, dim=0, out=sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         select()
@@ -220,7 +222,7 @@ def main():
             sel_flushed.append((a, b))
     torch.cuda.synchronize()
     sel_flush_ms = float(np.median([a.elapsed_time(b) for a, b in sel_flushed]))
-    del flush
+    del flush, sink
     sel_bytes = 2.0 * B * H * N * D * 2 + B * H * n * n + 4.0 * B * H * n * keep + 4.0 * B * H * n
 
     # ---- the dense comparator

@@ -48,7 +48,7 @@ int ni_for(int n) {  // elements per lane for a row of n blocks: 1, 2, 4, 8 or 1
 template <int D>
 void launch_pool(int BH, int N, int n, int block, float scale, const uint16_t* q, const uint16_t* k,
                  float* aq, float* ak, hipStream_t s) {
-  const dim3 grid(2 * BH * n);
+  const dim3 grid((2 * BH * n + 3) / 4);  // one wave per (tensor, head, block)
   if (block == 64)
     ba::pool_stats_kernel<D, 64><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
   else
@@ -59,8 +59,10 @@ template <int D, int NI>
 void launch_score_ni(int BH, int n, int keep, const float* aq, const float* ak, uint8_t* mask,
                      int32_t* idx, int32_t* cnt, float* score, hipStream_t s) {
   const int tiles = (n + ba::kScoreRows - 1) / ba::kScoreRows;
+  const int total = BH * tiles;
   const size_t smem = (size_t)ba::kScoreRows * n * sizeof(float);
-  ba::score_topk_kernel<D, NI><<<dim3(BH * tiles), 256, smem, s>>>(aq, ak, n, keep, mask, idx, cnt, score);
+  ba::score_topk_kernel<D, NI><<<dim3(round_up8(total)), ba::kScoreWaves * 64, smem, s>>>(
+      aq, ak, n, keep, mask, idx, cnt, score, total);
 }
 
 template <int D>
