@@ -172,9 +172,10 @@ def main():
           file=sys.stderr, flush=True)
 
     if args.copy_calibration:
-        # a plain copy of known size: reads 1 GiB and writes 1 GiB per dispatch
+        # a plain copy of known size in one elementwise dispatch (a uint8 ->
+        # int8 cast copy): reads 1 GiB and writes 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
+        dst = torch.empty(1 << 30, dtype=torch.int8, device=dev)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
