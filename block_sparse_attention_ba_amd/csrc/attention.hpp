@@ -117,9 +117,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   static_assert(!SPARSE || ROWS == BLK, "sparse tile must be one query block");
   static_assert((kChunk * CPR) % (64 * WAVES) == 0, "tile must split evenly over the waves");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TILE_BYTES];
-  uint8_t* Kbuf = smem;
-  uint8_t* Vbuf = smem + TILE_BYTES;
+  // two separate arrays: the compiler then sees that a copy into one does not
+  // write the other, and does not make the reads of V wait for the copy of K
+  __shared__ __attribute__((aligned(1024))) uint8_t Ktile[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vtile[TILE_BYTES];
+  uint8_t* const Kbuf = Ktile;
+  uint8_t* const Vbuf = Vtile;
 
   const int logical = xcd_remap(blockIdx.x, p.total);
   if (logical < 0) return;
@@ -136,15 +139,17 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   const uint16_t* Kh = p.k + head;
   const uint16_t* Vh = p.v + head;
 
-  // ---- chunk schedule
+  // ---- chunk schedule; the block lists are read through the constant
+  // address space (scalar loads, which never wait for the tile copies)
+  typedef const __attribute__((address_space(4))) int32_t* cidx_t;
   int n_chunks;
-  const int32_t* idx_row = nullptr;
+  cidx_t idx_row = nullptr;
   if constexpr (SPARSE) {
     const int row = bh * p.n_blocks + qt;
-    int c = p.cnt[row];
+    int c = ((cidx_t)p.cnt)[row];
     c = c < 0 ? 0 : (c > p.max_keep ? p.max_keep : c);
     n_chunks = c * SUBS;
-    idx_row = p.idx + (size_t)row * p.max_keep;
+    idx_row = (cidx_t)p.idx + (size_t)row * p.max_keep;
   } else {
     n_chunks = (N + kChunk - 1) / kChunk;
   }
