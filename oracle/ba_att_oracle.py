@@ -41,6 +41,11 @@ R7  the "oracle post-downsample attention map" is the full N x N attention
     pooled per block pair after the nonlinearity: the block log-mean-exp of
     the logits (the quantity R4 approximates) and, secondarily, the block
     mean of the row-softmax probabilities.
+R8  attention results over disjoint key sets (the parts of a split key
+    list, or a caller's external contribution such as a cached estimate of
+    the dropped blocks) recombine exactly in log space:
+      LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p;
+    an empty part has LSE_p = -inf and weight 0.
 
 Parity status: the oracle is pinned by closed forms, exact special cases and
 brute force (see the tests); parity with the paper's own equations is
@@ -71,6 +76,7 @@ __all__ = [
     "block_attention_rows",
     "dense_attention",
     "attention_oracle",
+    "merge_attention",
 ]
 
 
@@ -414,3 +420,33 @@ def attention_oracle(q_bits, k_bits, v_bits, mask, b: int, scale: float | None =
         else:
             res[(bi, hi)] = block_attention_rows(q, k, v, mask[bi, hi], b, scale, rows)
     return res
+
+
+# --------------------------------------------------------------------------
+# O7: recombination of attention over disjoint key sets
+# --------------------------------------------------------------------------
+
+def merge_attention(o_parts, lse_parts):
+    """Exact recombination of attention over disjoint key sets (reading R8).
+
+    [FlashBlock review, "Core claim" / "What carries the argument"]: the
+    softmax of a row over the union of disjoint key sets is assembled from
+    each set's normalised output and log-normaliser.  With LSE_p = ln Z_p and
+    O_p = (1/Z_p) sum_{t in T_p} e^{x_t} v_t, the union has Z = sum_p Z_p, so
+    LSE = ln sum_p e^{LSE_p} and O = sum_p (Z_p/Z) O_p.
+
+    o_parts [P, ..., D], lse_parts [P, ...].  Parts with LSE_p = -inf are
+    empty (weight 0); when every part is empty, O = 0 and LSE = -inf.
+    """
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    nonempty = np.isfinite(m)
+    m0 = np.where(nonempty, m, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m0), 0.0)  # Z_p / e^m
+    z = w.sum(axis=0)
+    z1 = np.where(nonempty, z, 1.0)
+    lse = np.where(nonempty, m0 + np.log(z1), -np.inf)
+    O = (w[..., None] * o_parts).sum(axis=0) / z1[..., None]
+    O = np.where(nonempty[..., None], O, 0.0)
+    return O, lse

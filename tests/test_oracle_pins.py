@@ -366,6 +366,59 @@ def test_p9_log_space_merge_identity():
     assert np.allclose(O, np.exp(l1 - lm)[:, None] * O1 + np.exp(l2 - lm)[:, None] * O2, atol=1e-12)
 
 
+def test_merge_over_random_partition_is_textbook_attention():
+    # the keys of every row cut into three random disjoint sets; each set's
+    # attention is the textbook softmax over it, and the merge must give the
+    # textbook softmax over all keys
+    rng = np.random.default_rng(11)
+    N, D, scale = 40, 8, 0.4
+    q, k, v = (rng.standard_normal((N, D)) for _ in range(3))
+    part = rng.integers(0, 3, size=N)
+    rows = np.arange(0, N, 3)
+    Os, ls = [], []
+    for p in range(3):
+        keys = np.flatnonzero(part == p)
+        O, lse = orc.dense_attention(q, k[keys], v[keys], scale, rows=rows)
+        Os.append(O)
+        ls.append(lse)
+    Om, lm = orc.merge_attention(Os, ls)
+    Od, ld = orc.dense_attention(q, k, v, scale, rows=rows)
+    assert np.allclose(Om, Od, atol=1e-12) and np.allclose(lm, ld, atol=1e-12)
+
+
+def test_merge_sparse_plus_dropped_blocks_is_dense():
+    N, b, D = 80, 16, 8
+    q, k, v = _rand_head(N, D, 9)
+    scale = 0.3
+    mask, _, _, _, _ = orc.select_head(q, k, b, 0.5, scale)
+    O1, l1 = orc.block_attention(q, k, v, mask, b, scale)
+    O2, l2 = orc.block_attention(q, k, v, 1 - mask, b, scale)
+    Om, lm = orc.merge_attention([O1, O2], [l1, l2])
+    Od, ld = orc.dense_attention(q, k, v, scale)
+    assert np.allclose(Om, Od, atol=1e-12) and np.allclose(lm, ld, atol=1e-12)
+
+
+def test_merge_closed_forms_and_empty_parts():
+    rng = np.random.default_rng(12)
+    O1, O2 = rng.standard_normal((2, 5, 4))
+    a = rng.standard_normal(5)
+    # equal normalisers: the average, and ln 2 more
+    Om, lm = orc.merge_attention([O1, O2], [a, a])
+    assert np.allclose(Om, 0.5 * (O1 + O2), atol=1e-15) and np.allclose(lm, a + math.log(2), atol=1e-15)
+    # normalisers in ratio 3:1
+    Om, lm = orc.merge_attention([O1, O2], [a + math.log(3), a])
+    assert np.allclose(Om, 0.75 * O1 + 0.25 * O2, atol=1e-14) and np.allclose(lm, a + math.log(4), atol=1e-14)
+    # an empty part is the identity; a single part is the identity
+    ninf = np.full(5, -np.inf)
+    Om, lm = orc.merge_attention([O1, np.zeros((5, 4))], [a, ninf])
+    assert np.array_equal(Om, O1) and np.array_equal(lm, a)
+    Om, lm = orc.merge_attention([O1], [a])
+    assert np.allclose(Om, O1, atol=0) and np.array_equal(lm, a)
+    # every part empty: the empty sum
+    Om, lm = orc.merge_attention([O1, O2], [ninf, ninf])
+    assert np.all(Om == 0) and np.all(np.isneginf(lm))
+
+
 def test_p10_invariances():
     N, b, D = 64, 8, 8
     q, k, v = _rand_head(N, D, 6)
@@ -449,6 +502,27 @@ def test_planted_dropped_variance_product_fails_zero_mean_pin():
     bad = oracle_pair_score(Xq, Xk, scale, score=_score_without_vv)
     assert abs((good - exact) / lead - 1) < 0.02
     assert abs((bad - exact) / lead - 1) > 10
+
+
+def _merge_plain_average(o_parts, lse_parts):
+    return np.mean(o_parts, axis=0), np.log(np.sum(np.exp(lse_parts), axis=0))
+
+
+def _merge_unnormalised(o_parts, lse_parts):
+    lse = np.log(np.sum(np.exp(lse_parts), axis=0))
+    return np.sum(np.exp(np.asarray(lse_parts))[..., None] * np.asarray(o_parts), axis=0), lse
+
+
+@pytest.mark.parametrize("merge", [_merge_plain_average, _merge_unnormalised])
+def test_planted_merge_mistakes_fail_the_partition_pin(merge):
+    N, b, D = 80, 16, 8
+    q, k, v = _rand_head(N, D, 9)
+    mask, _, _, _, _ = orc.select_head(q, k, b, 0.5, 0.3)
+    O1, l1 = orc.block_attention(q, k, v, mask, b, 0.3)
+    O2, l2 = orc.block_attention(q, k, v, 1 - mask, b, 0.3)
+    Om, _ = merge([O1, O2], [l1, l2])
+    Od, _ = orc.dense_attention(q, k, v, 0.3)
+    assert not np.allclose(Om, Od, atol=1e-6)
 
 
 def test_empty_mask_row_is_the_empty_sum():
