@@ -17,7 +17,8 @@ BA_BF16, BA_F32 = 0, 1
 
 __all__ = [
     "load", "num_blocks", "keep_count", "select_workspace_bytes", "select", "mask_to_index",
-    "forward", "dense", "ba_attention",
+    "forward", "forward_split", "forward_split_workspace_bytes", "merge", "forward_ext", "dense",
+    "ba_attention",
 ]
 
 
@@ -146,6 +147,83 @@ def forward(q, k, v, idx, cnt, block: int, scale: float | None = None,
                                       k.data_ptr(), v.data_ptr(), idx.data_ptr(), cnt.data_ptr(),
                                       int(idx.shape[3]), out.data_ptr(), code,
                                       lse.data_ptr() if lse is not None else None, _stream(q)))
+    return out, lse
+
+
+def _forward_args(q, k, v, idx, cnt, block):
+    B, H, N, D = _qkv_shape(q)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, 4)
+        if tuple(t.shape) != (B, H, N, D):
+            raise ValueError(f"{name} must have the shape of q")
+    _need(idx, "idx", torch.int32, 4)
+    _need(cnt, "cnt", torch.int32, 3)
+    n = num_blocks(N, block)
+    if tuple(idx.shape[:3]) != (B, H, n) or tuple(cnt.shape) != (B, H, n):
+        raise ValueError("idx/cnt must be [B,H,n,max_keep] / [B,H,n]")
+    return B, H, N, D
+
+
+def forward_split_workspace_bytes(B: int, H: int, N: int, D: int, n_split: int) -> int:
+    return int(_lib.load().ba_att_forward_split_workspace_bytes(B, H, N, D, n_split))
+
+
+def forward_split(q, k, v, idx, cnt, block: int, n_split: int, scale: float | None = None,
+                  out_dtype: torch.dtype = torch.float32, out=None, lse=None, return_lse: bool = True,
+                  workspace: torch.Tensor | None = None):
+    """Block-sparse attention with every row's block list cut into n_split
+    parts attended separately and merged exactly; returns (O, LSE)."""
+    B, H, N, D = _forward_args(q, k, v, idx, cnt, block)
+    out, lse, code = _out(q, out_dtype, out, lse, return_lse)
+    need = forward_split_workspace_bytes(B, H, N, D, n_split)
+    if need == 0:
+        raise ValueError("n_split must lie in [1, 64]")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(_lib.load().ba_att_forward_split(
+        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+        cnt.data_ptr(), int(idx.shape[3]), int(n_split), out.data_ptr(), code,
+        lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, lse
+
+
+def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+          out=None, lse=None, return_lse: bool = True):
+    """Exact log-space merge of attention results over disjoint key sets:
+    o_parts fp32 [P,B,H,N,D], lse_parts fp32 [P,B,H,N] -> (O, LSE)."""
+    _need(o_parts, "o_parts", torch.float32, 5)
+    _need(lse_parts, "lse_parts", torch.float32, 4)
+    P, B, H, N, D = (int(x) for x in o_parts.shape)
+    if tuple(lse_parts.shape) != (P, B, H, N):
+        raise ValueError("lse_parts must be [P,B,H,N]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=out_dtype, device=o_parts.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    code = BA_F32 if out_dtype == torch.float32 else BA_BF16
+    _check(_lib.load().ba_att_merge(B, H, N, D, P, o_parts.data_ptr(), lse_parts.data_ptr(), out.data_ptr(),
+                                    code, lse.data_ptr() if lse is not None else None, _stream(o_parts)))
+    return out, lse
+
+
+def forward_ext(q, k, v, idx, cnt, block: int, o_ext: torch.Tensor, lse_ext: torch.Tensor,
+                scale: float | None = None, out_dtype: torch.dtype = torch.float32, out=None, lse=None,
+                return_lse: bool = True):
+    """Block-sparse attention merged with an external attention result
+    (o_ext fp32 [B,H,N,D], lse_ext fp32 [B,H,N]) over a disjoint key set."""
+    B, H, N, D = _forward_args(q, k, v, idx, cnt, block)
+    _need(o_ext, "o_ext", torch.float32, 4)
+    _need(lse_ext, "lse_ext", torch.float32, 3)
+    if tuple(o_ext.shape) != (B, H, N, D) or tuple(lse_ext.shape) != (B, H, N):
+        raise ValueError("o_ext/lse_ext must be [B,H,N,D] / [B,H,N]")
+    out, lse, code = _out(q, out_dtype, out, lse, return_lse)
+    _check(_lib.load().ba_att_forward_ext(
+        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+        cnt.data_ptr(), int(idx.shape[3]), o_ext.data_ptr(), lse_ext.data_ptr(), out.data_ptr(), code,
+        lse.data_ptr() if lse is not None else None, _stream(q)))
     return out, lse
 
 

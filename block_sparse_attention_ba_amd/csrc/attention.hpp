@@ -47,9 +47,19 @@ struct AttnParams {
   int N;
   int n_blocks;   // key blocks (sparse) -- also the number of query blocks
   int n_qtiles;   // query tiles per head
-  int total;      // BH * n_qtiles
+  int total;      // BH * n_qtiles * n_split
   int max_keep;
   float scale_log2;  // softmax scale * log2(e)
+  // split key lists: every row's chunk list is cut into n_split contiguous
+  // parts; part p writes its (O, LSE) at o + p*o_part_stride and
+  // lse + p*lse_part_stride (elements).  n_split = 1: no split.
+  int n_split;
+  size_t o_part_stride;
+  size_t lse_part_stride;
+  // optional external contribution (fp32 O [BH,N,D], natural-log LSE [BH,N])
+  // over another key set, merged into the result in log space
+  const float* o_ext;
+  const float* lse_ext;
 };
 
 constexpr int kChunk = 64;  // keys per LDS chunk
@@ -126,8 +136,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
   const int logical = xcd_remap(blockIdx.x, p.total);
   if (logical < 0) return;
-  const int bh = logical / p.n_qtiles;
-  const int qt = logical - bh * p.n_qtiles;
+  const int tile = logical / p.n_split;      // the parts of a tile are neighbours
+  const int part = logical - tile * p.n_split;
+  const int bh = tile / p.n_qtiles;
+  const int qt = tile - bh * p.n_qtiles;
   const int N = p.N;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -176,7 +188,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     voff_v[j] = r * ROW_BYTES + v_slot<CPR>(r, s) * 16;
   }
   auto tile_rsrc = [&](const uint16_t* src, int k0) {
-    const int rows = k0 < 0 ? 0 : min(kChunk, N - k0);
+    // (a chunk may start past N: the second half of a 128-key tail block with
+    // at most 64 rows; its count must clamp at 0, as a negative count would
+    // wrap to an unbounded resource)
+    const int rows = k0 < 0 ? 0 : max(0, min(kChunk, N - k0));
     return make_rsrc(src + (size_t)(k0 < 0 ? 0 : k0) * D, rows * ROW_BYTES);
   };
 
@@ -220,13 +235,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   float l_run = 0.f;
   const float sl2 = p.scale_log2;
 
-  int k0_next = n_chunks > 0 ? chunk_start(0) : 0;
-  if (n_chunks > 0) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
+  // this workgroup's part of the chunk list
+  const int per_part = (n_chunks + p.n_split - 1) / p.n_split;
+  const int c_begin = min(n_chunks, part * per_part);
+  const int c_end = min(n_chunks, c_begin + per_part);
 
-  for (int c = 0; c < n_chunks; ++c) {
+  int k0_next = c_begin < c_end ? chunk_start(c_begin) : 0;
+  if (c_begin < c_end) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
+
+  for (int c = c_begin; c < c_end; ++c) {
     const int k0 = k0_next;
-    const int valid = k0 < 0 ? 0 : min(kChunk, N - k0);
-    if (c + 1 < n_chunks) k0_next = chunk_start(c + 1);
+    const int valid = k0 < 0 ? 0 : max(0, min(kChunk, N - k0));
+    if (c + 1 < c_end) k0_next = chunk_start(c + 1);
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(c) landed
     __syncthreads();  // K(c) visible to all waves; every wave is done with V(c-1)
@@ -298,7 +318,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(c) landed
     __syncthreads();  // V(c) visible; every wave is done with K(c)
-    if (c + 1 < n_chunks) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
+    if (c + 1 < c_end) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
 
     // O^T (D x 32 queries) += V^T P^T, V operands read one step ahead
     bf16x8 vcur[DT];
@@ -321,35 +341,96 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     }
   }
 
-  // ---- epilogue
+  // ---- epilogue: LSE (log2 domain) and the factor of oacc in the output
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qrow < N) {
-    if (p.lse != nullptr && g == 0) {
-      p.lse[(size_t)bh * N + qrow] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
+  float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -__builtin_inff();
+  float w_own = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  float w_ext = 0.f;
+  const size_t row = (size_t)bh * N + qrow;
+  if (p.o_ext != nullptr && qrow < N) {
+    // merge with the external (O, LSE): weights Z_own/Z and Z_ext/Z
+    const float le2 = p.lse_ext[row] * 1.44269504088896340736f;
+    const float M = fmaxf(lse2, le2);
+    if (M != -__builtin_inff()) {
+      const float a = lse2 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(lse2 - M);
+      const float b = le2 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(le2 - M);
+      const float L = a + b;
+      w_own *= a / L;
+      w_ext = b / L;
+      lse2 = M + log2f(L);
     }
-    if constexpr (OUT_F32) {
-      float* Orow = reinterpret_cast<float*>(p.o) + head + (size_t)qrow * D;
+  }
+  if (qrow < N) {
+    if (p.lse != nullptr && g == 0)
+      p.lse[part * p.lse_part_stride + row] = lse2 * 0.69314718055994530942f;  // -inf stays -inf
+    // this lane's 4-value groups: d = dt*32 + 8j + 4g .. +3 (no lambda here:
+    // capturing oacc, sized by a template parameter, drops the launch stub)
+    const float* Erow = w_ext != 0.f ? p.o_ext + row * D : nullptr;
 #pragma unroll
-      for (int d = 0; d < DT; ++d)
+    for (int d = 0; d < DT; ++d)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 v4 = {oacc[d][4 * j] * inv, oacc[d][4 * j + 1] * inv, oacc[d][4 * j + 2] * inv,
-                      oacc[d][4 * j + 3] * inv};
-          *reinterpret_cast<f32x4*>(Orow + d * 32 + 8 * j + 4 * g) = v4;
-        }
-    } else {
-      uint16_t* Orow = reinterpret_cast<uint16_t*>(p.o) + head + (size_t)qrow * D;
-#pragma unroll
-      for (int d = 0; d < DT; ++d)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
+        const int dd = d * 32 + 8 * j + 4 * g;
+        f32x4 v4 = {oacc[d][4 * j] * w_own, oacc[d][4 * j + 1] * w_own, oacc[d][4 * j + 2] * w_own,
+                    oacc[d][4 * j + 3] * w_own};
+        if (Erow != nullptr) v4 += *reinterpret_cast<const f32x4*>(Erow + dd) * w_ext;
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + part * p.o_part_stride + row * D + dd) = v4;
+        } else {
           u32x2 w;
-          w[0] = pack_bf16x2(oacc[d][4 * j] * inv, oacc[d][4 * j + 1] * inv);
-          w[1] = pack_bf16x2(oacc[d][4 * j + 2] * inv, oacc[d][4 * j + 3] * inv);
-          *reinterpret_cast<u32x2*>(Orow + d * 32 + 8 * j + 4 * g) = w;
+          w[0] = pack_bf16x2(v4[0], v4[1]);
+          w[1] = pack_bf16x2(v4[2], v4[3]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + part * p.o_part_stride + row * D + dd) = w;
         }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact log-space merge of P attention results over disjoint key sets:
+//   LSE = ln sum_p e^{LSE_p},  O = sum_p e^{LSE_p - LSE} O_p
+// (a part with LSE_p = -inf weighs 0; all parts empty: O = 0, LSE = -inf).
+// One wave per row; lanes hold consecutive fp32 pairs (D = 128) or single
+// values (D = 64) of the row, so every part's row is one coalesced read.
+// ---------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_parts,
+                                                    const float* __restrict__ lse_parts, int n_parts,
+                                                    size_t rows, void* __restrict__ o,
+                                                    float* __restrict__ lse) {
+  constexpr int E = D / 64;  // values per lane
+  const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  float M = -__builtin_inff();
+  for (int q = 0; q < n_parts; ++q) M = fmaxf(M, lse_parts[q * rows + r]);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  if (M != -__builtin_inff()) {
+    for (int q = 0; q < n_parts; ++q) {
+      const float lq = lse_parts[q * rows + r];
+      if (lq == -__builtin_inff()) continue;
+      const float w = __builtin_amdgcn_exp2f((lq - M) * 1.44269504088896340736f);
+      L += w;
+      const float* src = o_parts + (q * rows + r) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(w, src[e], acc[e]);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  if (lse != nullptr && lane == 0) lse[r] = L > 0.f ? M + logf(L) : -__builtin_inff();
+  if constexpr (OUT_F32) {
+    float* dst = reinterpret_cast<float*>(o) + r * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = acc[e] * inv;
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(o) + r * D + lane * E;
+    if constexpr (E == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      dst[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
     }
   }
 }

@@ -164,21 +164,39 @@ int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* 
   return finish_launch();
 }
 
-int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
-                   const void* q, const void* k, const void* v, const int32_t* block_idx,
-                   const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
-                   float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxSplit = 64;
+
+// Checks of the arguments every forward variant shares.
+ba_status check_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, const void* q,
+                        const void* k, const void* v, const int32_t* block_idx, const int32_t* block_cnt,
+                        int32_t max_keep) {
   ba_status st = check_shape(B, H, N, D);
   if (st != BA_OK) return st;
-  if (!q || !k || !v || !block_idx || !block_cnt || !o) return BA_ERR_INVALID_ARG;
-  if (o_dtype != BA_BF16 && o_dtype != BA_F32) return BA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !block_idx || !block_cnt) return BA_ERR_INVALID_ARG;
   if (block != 64 && block != 128) return BA_ERR_UNSUPPORTED;
   if (max_keep < 1) return BA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(block_idx, 4) || !aligned(block_cnt, 4) || (lse && !aligned(lse, 4)))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(block_idx, 4) ||
+      !aligned(block_cnt, 4))
     return BA_ERR_INVALID_ARG;
+  if ((long long)B * H * num_blocks(N, block) * max_keep >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  return BA_OK;
+}
+
+// Sparse forward into o (o_f32: fp32, else bf16) and lse, cutting every
+// row's chunk list into n_split parts written at the given strides, and
+// merging an optional external contribution.
+ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                         const void* q, const void* k, const void* v, const int32_t* block_idx,
+                         const int32_t* block_cnt, int32_t max_keep, int n_split, void* o, bool o_f32,
+                         float* lse, size_t o_stride, size_t lse_stride, const float* o_ext,
+                         const float* lse_ext, hipStream_t s) {
   const int n = num_blocks(N, block);
-  if ((long long)B * H * n * max_keep >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  const long long total = (long long)B * H * n * n_split;
+  if (total >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
   ba::AttnParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -190,19 +208,109 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
   p.N = N;
   p.n_blocks = n;
   p.n_qtiles = n;
-  p.total = B * H * n;
+  p.total = (int)total;
   p.max_keep = max_keep;
   p.scale_log2 = resolve_scale(scale, D) * 1.44269504088896340736f;
-  const bool f32 = o_dtype == BA_F32;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  p.n_split = n_split;
+  p.o_part_stride = o_stride;
+  p.lse_part_stride = lse_stride;
+  p.o_ext = o_ext;
+  p.lse_ext = lse_ext;
   if (D == 128) {
-    if (block == 64) launch_attn<128, 2, 64, true>(p, f32, s);
-    else launch_attn<128, 4, 128, true>(p, f32, s);
+    if (block == 64) launch_attn<128, 2, 64, true>(p, o_f32, s);
+    else launch_attn<128, 4, 128, true>(p, o_f32, s);
   } else {
-    if (block == 64) launch_attn<64, 2, 64, true>(p, f32, s);
-    else launch_attn<64, 4, 128, true>(p, f32, s);
+    if (block == 64) launch_attn<64, 2, 64, true>(p, o_f32, s);
+    else launch_attn<64, 4, 128, true>(p, o_f32, s);
   }
   return finish_launch();
+}
+
+template <int D>
+void launch_merge_d(const float* o_parts, const float* lse_parts, int n_parts, size_t rows, void* o,
+                    bool o_f32, float* lse, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (o_f32)
+    ba::merge_kernel<D, true><<<grid, 256, 0, s>>>(o_parts, lse_parts, n_parts, rows, o, lse);
+  else
+    ba::merge_kernel<D, false><<<grid, 256, 0, s>>>(o_parts, lse_parts, n_parts, rows, o, lse);
+}
+
+void launch_merge(int D, const float* o_parts, const float* lse_parts, int n_parts, size_t rows, void* o,
+                  bool o_f32, float* lse, hipStream_t s) {
+  if (D == 128) launch_merge_d<128>(o_parts, lse_parts, n_parts, rows, o, o_f32, lse, s);
+  else launch_merge_d<64>(o_parts, lse_parts, n_parts, rows, o, o_f32, lse, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                   const void* q, const void* k, const void* v, const int32_t* block_idx,
+                   const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
+                   float* lse, void* stream) {
+  ba_status st = check_forward(B, H, N, D, block, q, k, v, block_idx, block_cnt, max_keep);
+  if (st != BA_OK) return st;
+  if (!o || (o_dtype != BA_BF16 && o_dtype != BA_F32)) return BA_ERR_INVALID_ARG;
+  if (!aligned(o, 16) || (lse && !aligned(lse, 4))) return BA_ERR_INVALID_ARG;
+  return launch_forward(B, H, N, D, block, scale, q, k, v, block_idx, block_cnt, max_keep, 1, o,
+                        o_dtype == BA_F32, lse, 0, 0, nullptr, nullptr, static_cast<hipStream_t>(stream));
+}
+
+size_t ba_att_forward_split_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t n_split) {
+  if (check_shape(B, H, N, D) != BA_OK || n_split < 1 || n_split > kMaxSplit) return 0;
+  return (size_t)n_split * B * H * N * (size_t)(D + 1) * sizeof(float);
+}
+
+int ba_att_forward_split(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                         const void* q, const void* k, const void* v, const int32_t* block_idx,
+                         const int32_t* block_cnt, int32_t max_keep, int32_t n_split, void* o,
+                         int32_t o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  ba_status st = check_forward(B, H, N, D, block, q, k, v, block_idx, block_cnt, max_keep);
+  if (st != BA_OK) return st;
+  if (!o || (o_dtype != BA_BF16 && o_dtype != BA_F32)) return BA_ERR_INVALID_ARG;
+  if (!aligned(o, 16) || (lse && !aligned(lse, 4))) return BA_ERR_INVALID_ARG;
+  if (n_split < 1 || n_split > kMaxSplit) return BA_ERR_INVALID_ARG;
+  const size_t need = ba_att_forward_split_workspace_bytes(B, H, N, D, n_split);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return BA_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * H * N;
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = o_parts + (size_t)n_split * rows * D;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_forward(B, H, N, D, block, scale, q, k, v, block_idx, block_cnt, max_keep, n_split, o_parts,
+                      true, lse_parts, rows * D, rows, nullptr, nullptr, s);
+  if (st != BA_OK) return st;
+  launch_merge(D, o_parts, lse_parts, n_split, rows, o, o_dtype == BA_F32, lse, s);
+  return finish_launch();
+}
+
+int ba_att_merge(int32_t B, int32_t H, int32_t N, int32_t D, int32_t n_parts, const float* o_parts,
+                 const float* lse_parts, void* o, int32_t o_dtype, float* lse, void* stream) {
+  ba_status st = check_shape(B, H, N, D);
+  if (st != BA_OK) return st;
+  if (n_parts < 1 || n_parts > kMaxSplit || !o_parts || !lse_parts || !o) return BA_ERR_INVALID_ARG;
+  if (o_dtype != BA_BF16 && o_dtype != BA_F32) return BA_ERR_INVALID_ARG;
+  if (!aligned(o_parts, 16) || !aligned(lse_parts, 4) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+    return BA_ERR_INVALID_ARG;
+  if ((long long)n_parts * B * H * N * D >= (1ll << 40)) return BA_ERR_UNSUPPORTED;
+  launch_merge(D, o_parts, lse_parts, n_parts, (size_t)B * H * N, o, o_dtype == BA_F32, lse,
+               static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+int ba_att_forward_ext(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                       const void* q, const void* k, const void* v, const int32_t* block_idx,
+                       const int32_t* block_cnt, int32_t max_keep, const float* o_ext,
+                       const float* lse_ext, void* o, int32_t o_dtype, float* lse, void* stream) {
+  ba_status st = check_forward(B, H, N, D, block, q, k, v, block_idx, block_cnt, max_keep);
+  if (st != BA_OK) return st;
+  if (!o || (o_dtype != BA_BF16 && o_dtype != BA_F32) || !o_ext || !lse_ext) return BA_ERR_INVALID_ARG;
+  if (!aligned(o, 16) || (lse && !aligned(lse, 4)) || !aligned(o_ext, 16) || !aligned(lse_ext, 4))
+    return BA_ERR_INVALID_ARG;
+  return launch_forward(B, H, N, D, block, scale, q, k, v, block_idx, block_cnt, max_keep, 1, o,
+                        o_dtype == BA_F32, lse, 0, 0, o_ext, lse_ext, static_cast<hipStream_t>(stream));
 }
 
 int ba_att_dense(int32_t B, int32_t H, int32_t N, int32_t D, float scale, const void* q,
@@ -226,6 +334,7 @@ int ba_att_dense(int32_t B, int32_t H, int32_t N, int32_t D, float scale, const 
   p.total = B * H * p.n_qtiles;
   p.max_keep = 0;
   p.scale_log2 = resolve_scale(scale, D) * 1.44269504088896340736f;
+  p.n_split = 1;
   const bool f32 = o_dtype == BA_F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128) launch_attn<128, 4, 64, false>(p, f32, s);

@@ -125,6 +125,49 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
                    const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
                    float* lse, void* stream);
 
+/* Split key lists (split-KV).  Every row's list of kept key blocks is cut
+ * into n_split contiguous parts (1 <= n_split <= 64); each part is attended
+ * by its own workgroup into fp32 partial results in the workspace, and the
+ * parts are then recombined exactly in log space (see ba_att_merge).  For
+ * shapes whose B*H*n workgroups cannot fill the device (few heads, short
+ * sequences); the result equals ba_att_forward's up to fp32 rounding.
+ * Workspace: ba_att_forward_split_workspace_bytes(...) bytes, 16-byte
+ * aligned: n_split partial outputs fp32 [B,H,N,D] then n_split partial LSEs
+ * fp32 [B,H,N].  Other arguments as in ba_att_forward. */
+size_t ba_att_forward_split_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t n_split);
+int ba_att_forward_split(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                         const void* q, const void* k, const void* v, const int32_t* block_idx,
+                         const int32_t* block_cnt, int32_t max_keep, int32_t n_split, void* o,
+                         int32_t o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Exact recombination of attention results over disjoint key sets
+ * (FlashBlock review, "Core claim" / "What carries the argument": a softmax
+ * row over a union of key sets assembled from each set's output and
+ * log-normaliser):
+ *   LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p.
+ * A part with LSE_p = -inf is empty and weighs 0; if every part is empty the
+ * row gets O = 0 and LSE = -inf.
+ *   o_parts    fp32 [n_parts,B,H,N,D], 16-byte aligned       (in)
+ *   lse_parts  fp32 [n_parts,B,H,N], natural log             (in)
+ *   o          [B,H,N,D] of o_dtype; lse fp32 [B,H,N] or NULL (out)
+ * 1 <= n_parts <= 64. */
+int ba_att_merge(int32_t B, int32_t H, int32_t N, int32_t D, int32_t n_parts, const float* o_parts,
+                 const float* lse_parts, void* o, int32_t o_dtype, float* lse, void* stream);
+
+/* Block-sparse attention merged with an external contribution: the caller's
+ * attention result (o_ext fp32 [B,H,N,D], lse_ext fp32 [B,H,N], natural log)
+ * over a key set disjoint from the kept blocks -- for instance a cached
+ * estimate of the dropped blocks, as in FlashBlock's sparse-plus-residual
+ * combination (FlashBlock review, "What carries the argument") -- is folded
+ * into the result as by ba_att_merge with two parts.  With o_ext/lse_ext the
+ * attention over the complementary blocks the result is dense attention.
+ * Other arguments as in ba_att_forward. */
+int ba_att_forward_ext(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                       const void* q, const void* k, const void* v, const int32_t* block_idx,
+                       const int32_t* block_cnt, int32_t max_keep, const float* o_ext,
+                       const float* lse_ext, void* o, int32_t o_dtype, float* lse, void* stream);
+
 /* Dense bidirectional attention softmax(scale*Q K^T) V with its LSE; the
  * comparator of the sparse pass.  Arguments as in ba_att_forward. */
 int ba_att_dense(int32_t B, int32_t H, int32_t N, int32_t D, float scale, const void* q,

@@ -51,9 +51,13 @@ def compare_masks(gpu_mask: np.ndarray, S: np.ndarray, oracle_mask: np.ndarray, 
 
 
 def max_abs(a, b) -> float:
+    """max |a - b|, where equal infinities count as equal and a NaN on
+    either side counts as an infinite error."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
+    if np.isnan(a).any() or np.isnan(b).any():
+        return math.inf
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
     with np.errstate(invalid="ignore"):
         d = np.where(both_inf, 0.0, np.abs(a - b))
-    return float(np.nanmax(d)) if d.size else 0.0
+    return float(np.max(d)) if d.size else 0.0

@@ -125,6 +125,44 @@ def test_forward_and_dense_reject_before_launch(lib):
     assert dense(B=1 << 16, H=1 << 8) == 2  # too many elements
 
 
+def test_split_merge_ext_reject_before_launch(lib):
+    assert lib.ba_att_forward_split_workspace_bytes(1, 2, 100, 64, 3) == 3 * 2 * 100 * 65 * 4
+    assert lib.ba_att_forward_split_workspace_bytes(1, 2, 100, 64, 0) == 0
+    assert lib.ba_att_forward_split_workspace_bytes(1, 2, 100, 64, 65) == 0
+    assert lib.ba_att_forward_split_workspace_bytes(1, 2, 100, 96, 2) == 0
+
+    def split(**kw):
+        a = dict(B=1, H=1, N=1024, D=128, block=64, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, mk=8,
+                 ns=2, o=FAKE, od=1, lse=None, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.ba_att_forward_split(a["B"], a["H"], a["N"], a["D"], a["block"], 0.0, a["q"], a["k"],
+                                        a["v"], a["idx"], a["cnt"], a["mk"], a["ns"], a["o"], a["od"],
+                                        a["lse"], a["ws"], a["wsb"], None)
+
+    assert split(ns=0) == 1 and split(ns=65) == 1
+    assert split(ws=None) == 3 and split(wsb=1024) == 3
+    assert split(v=None) == 1 and split(block=32) == 2 and split(o=FAKE + 4) == 1
+
+    def merge(**kw):
+        a = dict(B=1, H=2, N=64, D=64, P=2, op=FAKE, lp=FAKE, o=FAKE, od=0, lse=None)
+        a.update(kw)
+        return lib.ba_att_merge(a["B"], a["H"], a["N"], a["D"], a["P"], a["op"], a["lp"], a["o"], a["od"],
+                                a["lse"], None)
+
+    assert merge(P=0) == 1 and merge(P=65) == 1 and merge(op=None) == 1 and merge(lp=None) == 1
+    assert merge(D=96) == 2 and merge(od=3) == 1 and merge(op=FAKE + 8) == 1
+
+    def ext(**kw):
+        a = dict(B=1, H=1, N=1024, D=64, block=64, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, mk=8,
+                 oe=FAKE, le=FAKE, o=FAKE, od=1, lse=None)
+        a.update(kw)
+        return lib.ba_att_forward_ext(a["B"], a["H"], a["N"], a["D"], a["block"], 0.0, a["q"], a["k"], a["v"],
+                                      a["idx"], a["cnt"], a["mk"], a["oe"], a["le"], a["o"], a["od"], a["lse"],
+                                      None)
+
+    assert ext(oe=None) == 1 and ext(le=None) == 1 and ext(oe=FAKE + 4) == 1 and ext(D=80) == 2
+
+
 def test_mask_to_index_rejects_before_launch(lib):
     def m2i(**kw):
         a = dict(B=1, H=1, n=16, mask=FAKE, mk=16, idx=FAKE, cnt=FAKE)

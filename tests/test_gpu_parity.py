@@ -114,6 +114,10 @@ ATTN_CASES = [
     (1, 1, 50, 64, 64, 0.0),
     (1, 2, 1000, 64, 128, 0.5),
     (1, 1, 4096, 128, 64, 0.9),
+    # 128-key tail blocks of at most 64 rows: the second 64-key half starts
+    # past N and must copy nothing (in the last batch it is the tensor's end)
+    (2, 1, 777, 64, 128, 0.5),
+    (1, 2, 800, 128, 128, 0.0),
 ]
 
 
