@@ -57,7 +57,61 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
+    ap.add_argument("--skip-split", action="store_true", help="omit the split key-list measurement")
     return ap.parse_args()
+
+
+def split_kv_measurement(lib, dev, stream, warmup: int, reps: int) -> dict:
+    """Split key lists on a shape whose workgroups half-fill the device:
+    one head, N = 32768, D = 128, block 64 (512 query blocks of 2 waves) at
+    50% sparsity.  Times ba_att_forward against ba_att_forward_split."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_ba_amd import api
+    B, H, N, D, blk, sp = 1, 1, 32768, 128, 64, 0.5
+    g = torch.Generator(device=dev).manual_seed(20260519)
+    q, k, v = (torch.randn((B, H, N, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    n = lib.ba_att_num_blocks(N, blk)
+    keep = lib.ba_att_keep_count(n, sp)
+    ws = torch.empty(api.select_workspace_bytes(B, H, N, D, blk), dtype=torch.uint8, device=dev)
+    mask = torch.empty((B, H, n, n), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    sptr = stream.cuda_stream
+    assert lib.ba_att_select(B, H, N, D, blk, 0.0, sp, q.data_ptr(), k.data_ptr(), mask.data_ptr(),
+                             idx.data_ptr(), cnt.data_ptr(), None, ws.data_ptr(), ws.numel(), sptr) == 0
+    splits = (2, 4, 8)
+    sws = torch.empty(lib.ba_att_forward_split_workspace_bytes(B, H, N, D, max(splits)), dtype=torch.uint8,
+                      device=dev)
+
+    def run(ns):
+        if ns == 1:
+            return lib.ba_att_forward(B, H, N, D, blk, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      idx.data_ptr(), cnt.data_ptr(), keep, o.data_ptr(), 0, lse.data_ptr(), sptr)
+        return lib.ba_att_forward_split(B, H, N, D, blk, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        idx.data_ptr(), cnt.data_ptr(), keep, ns, o.data_ptr(), 0,
+                                        lse.data_ptr(), sws.data_ptr(), sws.numel(), sptr)
+
+    def timed(ns):
+        for _ in range(warmup):
+            assert run(ns) == 0
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            run(ns)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    res = {"shape": "B1 H1 N32768 D128 block 64, 50% sparsity (512 query blocks)", "unsplit_ms": timed(1)}
+    res["split_ms"] = {str(ns): round(timed(ns), 5) for ns in splits}
+    best = min(res["split_ms"].items(), key=lambda kv: kv[1])
+    res["unsplit_ms"] = round(res["unsplit_ms"], 5)
+    res["best_split"] = int(best[0])
+    res["speedup"] = round(res["unsplit_ms"] / best[1], 3)
+    return res
 
 
 def kept_tile_flops(mask, N: int, D: int, block: int) -> float:
@@ -109,9 +163,9 @@ def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the operator has no "
-              "multi-GPU path in this build; every head is independent, so a multi-GPU run "
-              "would shard (batch, head) pairs with no communication.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path; every head is independent, so a multi-GPU run would shard "
+              "(batch, head) pairs with no communication.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -243,6 +297,11 @@ def main():
         print(f"[bench] dense {dense_ms:.4f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s)",
               file=sys.stderr, flush=True)
 
+    split_kv = None
+    if not args.skip_split:
+        split_kv = split_kv_measurement(lib, dev, stream, args.warmup, max(5, args.steps // 2))
+        print(f"[bench] split key lists: {split_kv}", file=sys.stderr, flush=True)
+
     # ---- HBM traffic from the committed counter runs, if they match these kernels
     traffic = None
     src_hash = kernel_source_hash()
@@ -290,6 +349,7 @@ def main():
                             "achieved": round(sel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,
                             "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
+        "split_kv": split_kv,
         "kernel_source_hash": src_hash,
     }
     if not args.skip_cpu:
