@@ -191,8 +191,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     // (a chunk may start past N: the second half of a 128-key tail block with
     // at most 64 rows; its count must clamp at 0, as a negative count would
     // wrap to an unbounded resource)
-    const int rows = k0 < 0 ? 0 : max(0, min(kChunk, N - k0));
-    return make_rsrc(src + (size_t)(k0 < 0 ? 0 : k0) * D, rows * ROW_BYTES);
+    // The values are wave-uniform, but the clamp is selected as a vector
+    // med3; readfirstlane puts them back in scalar registers, else every copy
+    // is wrapped in a loop that re-establishes a uniform resource.
+    const int rows = __builtin_amdgcn_readfirstlane(k0 < 0 ? 0 : max(0, min(kChunk, N - k0)));
+    const int first = __builtin_amdgcn_readfirstlane(k0 < 0 ? 0 : k0);
+    return make_rsrc(src + (size_t)first * D, rows * ROW_BYTES);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), loaded once
