@@ -283,11 +283,15 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
           if (key >= valid) sacc[kt][r] = -__builtin_inff();
         }
     }
-    float mloc = fmaxf(sacc[0][0], sacc[0][1]);
+    // two chains of three-input maxima (v_max3_f32): 17 instructions for 32 values
+    float ma = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+    float mb = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[0][r], sacc[0][r + 1]));
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    for (int r = 3; r < 15; r += 2) {
+      ma = fmaxf(fmaxf(ma, sacc[0][r]), sacc[0][r + 1]);
+      mb = fmaxf(fmaxf(mb, sacc[1][r]), sacc[1][r + 1]);
+    }
+    float mloc = fmaxf(fmaxf(ma, sacc[0][15]), fmaxf(mb, sacc[1][15]));
     mloc = pair_max(mloc) * sl2;
     if (__any(mloc > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mloc);
