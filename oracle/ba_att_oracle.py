@@ -46,6 +46,13 @@ R8  attention results over disjoint key sets (the parts of a split key
     the dropped blocks) recombine exactly in log space:
       LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p;
     an empty part has LSE_p = -inf and weight 0.
+R9  the selection-quality diagnostics (full covariance vs diagonal vs no
+    correction, against the post-downsample maps of R7) compare maps row by
+    row: block recall = |top_keep(x) & top_keep(r)| / keep with both sets
+    taken by the norm-sort rule of R5, and Spearman's rho = the Pearson
+    correlation of tie-averaged ranks (0 when a row is constant, where rho
+    is undefined).  The uncorrected score is the first-order term of R4
+    alone, scale*<qm_I, km_J>.
 
 Parity status: the oracle is pinned by closed forms, exact special cases and
 brute force (see the tests); parity with the paper's own equations is
@@ -66,6 +73,9 @@ __all__ = [
     "block_stats",
     "compact_score",
     "compact_score_full_cov",
+    "uncorrected_score",
+    "average_ranks",
+    "rank_agreement",
     "norm_sort_row",
     "norm_sort",
     "cut_margins",
@@ -196,6 +206,13 @@ def compact_score_full_cov(Qb: list[np.ndarray], Kb: list[np.ndarray], scale: fl
     return S
 
 
+def uncorrected_score(qm: np.ndarray, km: np.ndarray, scale: float) -> np.ndarray:
+    """Diagnostic: the compact score without the covariance correction,
+    scale*<qm_I, km_J> -- the first-order term of reading R4 alone, i.e.
+    ranking blocks by the logits of their pooled queries and keys."""
+    return scale * (qm @ km.T)
+
+
 # --------------------------------------------------------------------------
 # O4: norm sorting into a block mask
 # --------------------------------------------------------------------------
@@ -224,6 +241,37 @@ def norm_sort(S: np.ndarray, keep: int) -> tuple[np.ndarray, np.ndarray, np.ndar
         idx[I] = kept
     cnt = np.full(nq, keep, dtype=np.int32)
     return mask, idx, cnt
+
+
+def average_ranks(x: np.ndarray) -> np.ndarray:
+    """1-based ranks of the entries of x, tied entries sharing the mean of
+    the ranks they span: rank_i = #{j: x_j < x_i} + (#{j: x_j = x_i} + 1)/2."""
+    x = np.asarray(x, dtype=np.float64)
+    less = (x[None, :] < x[:, None]).sum(axis=1)
+    equal = (x[None, :] == x[:, None]).sum(axis=1)
+    return less + (equal + 1) / 2.0
+
+
+def rank_agreement(x_row: np.ndarray, r_row: np.ndarray, keep: int) -> tuple[float, float]:
+    """Selection-quality diagnostic of one query-block row (reading R9).
+
+    [BA-Att review, "Core claim": the pre-downsampled scores stand in for the
+    post-downsample map; referee report: how well the diagonal approximation
+    ranks blocks is not measured].  Returns (recall, rho):
+      recall = |kept(x) & kept(r)| / keep, kept by the norm-sort rule;
+      rho    = Pearson correlation of average_ranks(x) and average_ranks(r),
+               0 when either row is constant.
+    """
+    kx = set(norm_sort_row(x_row, keep))
+    kr = set(norm_sort_row(r_row, keep))
+    recall = len(kx & kr) / keep
+    a = average_ranks(x_row)
+    b = average_ranks(r_row)
+    a = a - a.mean()
+    b = b - b.mean()
+    den = math.sqrt(float(np.sum(a * a)) * float(np.sum(b * b)))
+    rho = float(np.sum(a * b)) / den if den > 0 else 0.0
+    return recall, rho
 
 
 def cut_margins(S: np.ndarray, keep: int) -> np.ndarray:

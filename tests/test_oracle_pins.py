@@ -535,3 +535,87 @@ def test_empty_mask_row_is_the_empty_sum():
     assert np.all(np.isfinite(lse[:16])) and np.all(np.isfinite(lse[32:]))
     Or, lr = orc.block_attention_rows(q, k, v, mask, b, 0.5, [3, 20])
     assert np.all(Or[1] == 0) and np.isneginf(lr[1]) and np.allclose(Or[0], O[3])
+
+
+# ------------------------------------------------ selection-quality diagnostics
+
+def test_uncorrected_score_is_the_pooled_logit():
+    rng = np.random.default_rng(21)
+    N, b, D, scale = 70, 16, 5, 0.4
+    q, k = rng.normal(size=(N, D)), rng.normal(size=(N, D))
+    qm, qv = orc.block_stats(q, b)
+    km, kv = orc.block_stats(k, b)
+    S0 = orc.uncorrected_score(qm, km, scale)
+    n = orc.num_blocks(N, b)
+    for I in range(n):
+        for J in range(n):
+            mq = q[I * b:(I + 1) * b].mean(axis=0)
+            mk = k[J * b:(J + 1) * b].mean(axis=0)
+            assert abs(S0[I, J] - scale * sum(mq[c] * mk[c] for c in range(D))) < 1e-13
+    # the corrected score minus its three variance products is this score
+    assert np.allclose(orc.compact_score(qm, np.zeros_like(qv), km, np.zeros_like(kv), scale), S0,
+                       rtol=0, atol=1e-14)
+    assert np.all(orc.compact_score(qm, qv, km, kv, scale) > S0)  # the correction is a variance: >= 0
+
+
+def test_average_ranks_and_rank_agreement_closed_forms():
+    x = np.array([3.0, 1.0, 3.0, 2.0])
+    r = np.array([1.0, 2.0, 3.0, 4.0])
+    assert orc.average_ranks(x).tolist() == [3.5, 1.0, 3.5, 2.0]
+    # hand computation: centred ranks a = (1, -1.5, 1, -0.5), b = (-1.5, -0.5, 0.5, 1.5):
+    # sum ab = -1, sum a^2 = 4.5, sum b^2 = 5; kept(x, 2) = {0, 2}, kept(r, 2) = {2, 3}
+    rec, rho = orc.rank_agreement(x, r, 2)
+    assert rec == 0.5
+    assert abs(rho - (-1.0 / math.sqrt(22.5))) < 1e-15
+    rng = np.random.default_rng(22)
+    y = rng.normal(size=33)
+    assert orc.rank_agreement(y, y, 7) == (1.0, 1.0)
+    assert orc.rank_agreement(y, 3.0 * y + 1.0, 7) == (1.0, 1.0)  # monotone maps keep ranks
+    rec, rho = orc.rank_agreement(y, -y, 16)
+    assert rec == 0.0 and abs(rho + 1.0) < 1e-14
+    # a constant row has no ranking: rho is defined as 0, recall follows the tie rule
+    c = np.full(10, 2.5)
+    rec, rho = orc.rank_agreement(c, np.arange(10.0), 3)
+    assert rho == 0.0 and rec == 0.0  # kept(c) = {0, 1, 2} (ties to the lower index), kept(r) = {7, 8, 9}
+    rec, rho = orc.rank_agreement(c, -np.arange(10.0), 3)
+    assert rho == 0.0 and rec == 1.0  # kept(r) = {0, 1, 2}
+
+
+def test_spearman_matches_library_on_tied_rows():
+    import scipy.stats
+    rng = np.random.default_rng(23)
+    for trial in range(40):
+        n = int(rng.integers(5, 70))
+        x = np.round(rng.normal(size=n), 1)  # many ties
+        r = np.round(x + rng.normal(size=n), 1) if trial % 2 else np.round(rng.normal(size=n), 1)
+        _, rho = orc.rank_agreement(x, r, max(1, n // 3))
+        ref = scipy.stats.spearmanr(x, r).statistic
+        assert abs(rho - ref) < 1e-12, (trial, rho, ref)
+
+
+def test_recall_matches_bruteforce_sort():
+    rng = np.random.default_rng(24)
+    for trial in range(60):
+        n = int(rng.integers(2, 80))
+        keep = int(rng.integers(1, n + 1))
+        x = np.round(rng.normal(size=n), 1)
+        r = np.round(rng.normal(size=n), 1)
+        top = lambda v: set(np.lexsort((np.arange(n), -v))[:keep].tolist())  # value desc, index asc
+        rec, _ = orc.rank_agreement(x, r, keep)
+        assert rec == len(top(x) & top(r)) / keep
+
+
+def _ordinal_ranks(x):
+    out = np.empty(len(x))
+    out[np.argsort(x, kind="stable")] = np.arange(1, len(x) + 1)
+    return out
+
+
+def test_planted_ordinal_ranks_fail_the_library_pin(monkeypatch):
+    import scipy.stats
+    monkeypatch.setattr(orc, "average_ranks", _ordinal_ranks)
+    rng = np.random.default_rng(25)
+    x = np.round(rng.normal(size=40), 0)
+    r = np.round(x + rng.normal(size=40), 0)
+    _, rho = orc.rank_agreement(x, r, 10)
+    assert abs(rho - scipy.stats.spearmanr(x, r).statistic) > 1e-3
