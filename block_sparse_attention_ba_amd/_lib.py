@@ -29,6 +29,10 @@ SIGNATURES = [
     ("ba_att_forward_ext", ctypes.c_int,
      [_i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _i32, _p, _p]),
     ("ba_att_dense", ctypes.c_int, [_i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p]),
+    ("ba_att_block_map", ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _p]),
+    ("ba_att_score_full_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
+    ("ba_att_score_full", ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _sz, _p]),
+    ("ba_att_rank_agreement", ctypes.c_int, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     ("ba_att_status_string", ctypes.c_char_p, [ctypes.c_int]),
 ]
 

@@ -18,7 +18,7 @@ BA_BF16, BA_F32 = 0, 1
 __all__ = [
     "load", "num_blocks", "keep_count", "select_workspace_bytes", "select", "mask_to_index",
     "forward", "forward_split", "forward_split_workspace_bytes", "merge", "forward_ext", "dense",
-    "ba_attention",
+    "ba_attention", "block_map", "score_full_workspace_bytes", "score_full", "rank_agreement",
 ]
 
 
@@ -248,6 +248,69 @@ def ba_attention(q, k, v, block: int, sparsity: float, scale: float | None = Non
     mask, idx, cnt = select(q, k, block, sparsity, scale)
     out, lse = forward(q, k, v, idx, cnt, block, scale, out_dtype=out_dtype)
     return out, lse, mask
+
+
+def block_map(q, k, block: int, lse: torch.Tensor | None = None, scale: float | None = None):
+    """Exact post-downsample maps of the full attention: M_lme fp32 [B,H,n,n]
+    (block log-mean-exp of the logits) and, given the rows' natural-log LSE
+    over all keys (fp32 [B,H,N], e.g. from dense), M_prob fp32 [B,H,n,n]
+    (block mean of the softmax probabilities); M_prob is None without lse."""
+    B, H, N, D = _qkv_shape(q)
+    _need(k, "k", torch.bfloat16, 4)
+    if tuple(k.shape) != (B, H, N, D):
+        raise ValueError("k must have the shape of q")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be [B,H,N]")
+    n = num_blocks(N, block)
+    m_lme = torch.empty((B, H, n, n), dtype=torch.float32, device=q.device)
+    m_prob = torch.empty_like(m_lme) if lse is not None else None
+    _check(_lib.load().ba_att_block_map(
+        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(),
+        lse.data_ptr() if lse is not None else None, m_lme.data_ptr(),
+        m_prob.data_ptr() if m_prob is not None else None, _stream(q)))
+    return m_lme, m_prob
+
+
+def score_full_workspace_bytes(B: int, H: int, N: int, D: int, block: int) -> int:
+    return int(_lib.load().ba_att_score_full_workspace_bytes(B, H, N, D, block))
+
+
+def score_full(q, k, block: int, scale: float | None = None, workspace: torch.Tensor | None = None):
+    """Block scores with full block covariances and without any correction:
+    returns (S_full, S_mean), fp32 [B,H,n,n] each."""
+    B, H, N, D = _qkv_shape(q)
+    _need(k, "k", torch.bfloat16, 4)
+    if tuple(k.shape) != (B, H, N, D):
+        raise ValueError("k must have the shape of q")
+    n = num_blocks(N, block)
+    need = score_full_workspace_bytes(B, H, N, D, block)
+    if need == 0:
+        raise RuntimeError("BA-Att call failed: unsupported shape for the full-covariance score")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    s_full = torch.empty((B, H, n, n), dtype=torch.float32, device=q.device)
+    s_mean = torch.empty_like(s_full)
+    _check(_lib.load().ba_att_score_full(
+        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), s_full.data_ptr(),
+        s_mean.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return s_full, s_mean
+
+
+def rank_agreement(x: torch.Tensor, r: torch.Tensor, keep: int):
+    """Per row of two block maps fp32 [B,H,n,n]: (recall, rho) fp32 [B,H,n] --
+    overlap of the kept sets (norm-sort rule) / keep, and Spearman's rho."""
+    _need(x, "x", torch.float32, 4)
+    _need(r, "r", torch.float32, 4)
+    if x.shape != r.shape or x.shape[2] != x.shape[3]:
+        raise ValueError("x and r must be the same [B,H,n,n] shape")
+    B, H, n, _ = (int(v) for v in x.shape)
+    recall = torch.empty((B, H, n), dtype=torch.float32, device=x.device)
+    rho = torch.empty_like(recall)
+    _check(_lib.load().ba_att_rank_agreement(B, H, n, int(keep), x.data_ptr(), r.data_ptr(),
+                                             recall.data_ptr(), rho.data_ptr(), _stream(x)))
+    return recall, rho
 
 
 def default_scale(D: int) -> float:

@@ -9,6 +9,7 @@
 
 #include "ba_att.h"
 #include "attention.hpp"
+#include "diagnostics.hpp"
 #include "select.hpp"
 
 namespace {
@@ -339,6 +340,161 @@ int ba_att_dense(int32_t B, int32_t H, int32_t N, int32_t D, float scale, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128) launch_attn<128, 4, 64, false>(p, f32, s);
   else launch_attn<64, 4, 64, false>(p, f32, s);
+  return finish_launch();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ diagnostics
+namespace {
+
+constexpr int kMaxMapParts = 4096;  // n * waves per workgroup: 12 bytes each of LDS
+
+template <int D, int WAVES, int BLK>
+void launch_block_map(const ba::MapParams& p, hipStream_t s) {
+  const size_t smem = (size_t)p.n_blocks * WAVES * 3 * sizeof(float);
+  ba::block_map_kernel<D, WAVES, BLK><<<dim3(round_up8(p.total)), WAVES * 64, smem, s>>>(p);
+}
+
+// Split of the full-covariance product: part 0 covers the D mean channels
+// (so it is the uncorrected score), parts 1..P-1 the 2T moment entries in
+// chunks of k_chunk (a multiple of 8), enough parts for ~2048 workgroups.
+struct FullPlan {
+  int kf, k_chunk, parts, tiles;
+};
+
+FullPlan full_plan(int BH, int n, int D) {
+  FullPlan f;
+  f.kf = D + D * (D + 1);
+  f.tiles = (n + 63) / 64;
+  const long long tiles = (long long)BH * f.tiles * f.tiles;
+  long long split = (2048 + tiles - 1) / tiles;
+  if (split < 1) split = 1;
+  if (split > 16) split = 16;
+  const int rest = f.kf - D;
+  f.k_chunk = (int)(((rest + split - 1) / split + 7) / 8 * 8);
+  f.parts = 1 + (rest + f.k_chunk - 1) / f.k_chunk;
+  return f;
+}
+
+template <int D>
+void launch_moments(int BH, int N, int n, int block, float scale, const uint16_t* q, const uint16_t* k,
+                    float* aqf, float* akf, hipStream_t s) {
+  const dim3 grid((unsigned)(2 * BH * n));
+  if (block == 64)
+    ba::moments_kernel<D, 64><<<grid, 256, 0, s>>>(q, k, aqf, akf, N, n, BH, scale);
+  else
+    ba::moments_kernel<D, 128><<<grid, 256, 0, s>>>(q, k, aqf, akf, N, n, BH, scale);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ba_att_block_map(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                     const void* q, const void* k, const float* lse, float* m_lme, float* m_prob,
+                     void* stream) {
+  ba_status st = check_shape(B, H, N, D);
+  if (st != BA_OK) return st;
+  if (!q || !k || !m_lme || ((lse == nullptr) != (m_prob == nullptr))) return BA_ERR_INVALID_ARG;
+  if (block != 64 && block != 128) return BA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(m_lme, 4) || (lse && !aligned(lse, 4)) ||
+      (m_prob && !aligned(m_prob, 4)))
+    return BA_ERR_INVALID_ARG;
+  const int n = num_blocks(N, block);
+  const int waves = block / 32;
+  if ((long long)n * waves > kMaxMapParts) return BA_ERR_UNSUPPORTED;
+  const long long total = (long long)B * H * n;
+  if (total * n >= (1ll << 40) || total >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  ba::MapParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.lse = lse;
+  p.m_lme = m_lme;
+  p.m_prob = m_prob;
+  p.N = N;
+  p.n_blocks = n;
+  p.total = (int)total;
+  p.scale_log2 = resolve_scale(scale, D) * 1.44269504088896340736f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 128) {
+    if (block == 64) launch_block_map<128, 2, 64>(p, s);
+    else launch_block_map<128, 4, 128>(p, s);
+  } else {
+    if (block == 64) launch_block_map<64, 2, 64>(p, s);
+    else launch_block_map<64, 4, 128>(p, s);
+  }
+  return finish_launch();
+}
+
+size_t ba_att_score_full_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block) {
+  if (check_shape(B, H, N, D) != BA_OK || (block != 64 && block != 128)) return 0;
+  const int n = num_blocks(N, block);
+  if (n > kMaxSelectBlocks) return 0;
+  const int BH = B * H;
+  const FullPlan f = full_plan(BH, n, D);
+  return (2 * (size_t)BH * n * f.kf + (size_t)f.parts * BH * n * n) * sizeof(float);
+}
+
+int ba_att_score_full(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                      const void* q, const void* k, float* s_full, float* s_mean, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  ba_status st = check_shape(B, H, N, D);
+  if (st != BA_OK) return st;
+  if (!q || !k || !s_full) return BA_ERR_INVALID_ARG;
+  if (block != 64 && block != 128) return BA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(s_full, 4) || (s_mean && !aligned(s_mean, 4)))
+    return BA_ERR_INVALID_ARG;
+  const int n = num_blocks(N, block);
+  if (n > kMaxSelectBlocks) return BA_ERR_UNSUPPORTED;
+  const size_t need = ba_att_score_full_workspace_bytes(B, H, N, D, block);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return BA_ERR_WORKSPACE;
+  const int BH = B * H;
+  const FullPlan f = full_plan(BH, n, D);
+  float* aqf = static_cast<float*>(workspace);
+  float* akf = aqf + (size_t)BH * n * f.kf;
+  float* parts = akf + (size_t)BH * n * f.kf;
+  const float sc = resolve_scale(scale, D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  if (D == 128) launch_moments<128>(BH, N, n, block, sc, q16, k16, aqf, akf, s);
+  else launch_moments<64>(BH, N, n, block, sc, q16, k16, aqf, akf, s);
+  ba::GemmParams g{};
+  g.a = aqf;
+  g.b = akf;
+  g.parts = parts;
+  g.n = n;
+  g.K = f.kf;
+  g.BH = BH;
+  g.n_tiles = f.tiles;
+  g.k_first = D;
+  g.k_chunk = f.k_chunk;
+  g.P = f.parts;
+  const long long wgs = (long long)f.parts * BH * f.tiles * f.tiles;
+  if (wgs >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  ba::gemm_nt_f32_kernel<<<dim3((unsigned)wgs), 256, 0, s>>>(g);
+  const size_t count = (size_t)BH * n * n;
+  const unsigned grid = (unsigned)((count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096);
+  ba::sum_parts_kernel<<<dim3(grid), 256, 0, s>>>(parts, f.parts, count, s_full, s_mean);
+  return finish_launch();
+}
+
+int ba_att_rank_agreement(int32_t B, int32_t H, int32_t n_blocks, int32_t keep, const float* x,
+                          const float* r, float* recall, float* rho, void* stream) {
+  if (B < 1 || H < 1 || n_blocks < 1 || keep < 1 || keep > n_blocks) return BA_ERR_INVALID_ARG;
+  if (!x || !r || !recall || !rho) return BA_ERR_INVALID_ARG;
+  if (!aligned(x, 4) || !aligned(r, 4) || !aligned(recall, 4) || !aligned(rho, 4)) return BA_ERR_INVALID_ARG;
+  if (n_blocks > ba::kAgreeMaxN) return BA_ERR_UNSUPPORTED;
+  const long long rows = (long long)B * H * n_blocks;
+  if (rows * n_blocks >= (1ll << 40) || rows >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ne = (n_blocks + 63) / 64;
+  if (ne <= 1) ba::rank_agree_kernel<1><<<grid, 256, 0, s>>>(x, r, (int)rows, n_blocks, keep, recall, rho);
+  else if (ne <= 2) ba::rank_agree_kernel<2><<<grid, 256, 0, s>>>(x, r, (int)rows, n_blocks, keep, recall, rho);
+  else if (ne <= 4) ba::rank_agree_kernel<4><<<grid, 256, 0, s>>>(x, r, (int)rows, n_blocks, keep, recall, rho);
+  else ba::rank_agree_kernel<8><<<grid, 256, 0, s>>>(x, r, (int)rows, n_blocks, keep, recall, rho);
   return finish_launch();
 }
 

@@ -173,6 +173,56 @@ int ba_att_forward_ext(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block
 int ba_att_dense(int32_t B, int32_t H, int32_t N, int32_t D, float scale, const void* q,
                  const void* k, const void* v, void* o, int32_t o_dtype, float* lse, void* stream);
 
+/* ---- selection-quality diagnostics -------------------------------------
+ * The review's "Core claim" and abstract have the diagonal-variance score
+ * stand in for the full covariance, and the pre-downsampled scores stand in
+ * for the post-downsample attention map; its referee report notes that
+ * neither approximation is quantified.  These calls measure both.  They are
+ * not on the attention path. */
+
+/* Exact post-downsample maps of full attention (the review's "oracle"
+ * post-downsample map), for x = scale*<q_s, k_t> over all tokens:
+ *   m_lme[b,h,I,J]  = ln( mean_{s in I, t in J} exp(x_st) )
+ *   m_prob[b,h,I,J] = mean_{s in I, t in J} exp(x_st - LSE_s)
+ * with LSE_s the natural-log normaliser of row s over all keys, passed in as
+ * `lse` (fp32 [B,H,N], e.g. ba_att_dense's).  lse and m_prob are both NULL
+ * (M_prob not computed) or both set.  m_lme, m_prob fp32 [B,H,n,n] (out).
+ * Cost: the score half of dense attention.  Supported: n*block/32 <= 4096
+ * (N <= 131072). */
+int ba_att_block_map(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                     const void* q, const void* k, const float* lse, float* m_lme, float* m_prob,
+                     void* stream);
+
+/* Block scores without the diagonal restriction and without any correction:
+ *   s_full[b,h,I,J] = scale*<qm_I, km_J>
+ *                     + scale^2/2 * ( <Cq_I, Ck_J>_F + km_J' Cq_I km_J + qm_I' Ck_J qm_I )
+ *   s_mean[b,h,I,J] = scale*<qm_I, km_J>            (optional, may be NULL)
+ * qm, km are block means and Cq, Ck the population (1/|I|) covariance
+ * matrices of the block's tokens.  s_full is the same second-cumulant score
+ * as ba_att_select's with the covariances kept whole.  Computed as one fp32
+ * product of augmented rows of D + D(D+1) entries (means, packed upper
+ * triangles of the second moments).  Workspace:
+ * ba_att_score_full_workspace_bytes(...) bytes, 16-byte aligned.  That is
+ * 2*B*H*n*(D + D(D+1))*4 bytes for the augmented rows (545 MB at
+ * B1 H32 N8192 D128 b64) plus the split-product parts.  Supported: n <= 512.
+ * Returns 0 bytes for an unsupported shape. */
+size_t ba_att_score_full_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block);
+int ba_att_score_full(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                      const void* q, const void* k, float* s_full, float* s_mean, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Row-by-row agreement of a block score map x with a reference map r (both
+ * fp32 [B,H,n,n]):
+ *   recall[b,h,I] = |kept(x row) & kept(r row)| / keep, where kept() is the
+ *                   norm-sort rule of ba_att_select (value descending, ties
+ *                   to the lower index, first `keep`);
+ *   rho[b,h,I]    = Spearman's rank correlation, the Pearson correlation of
+ *                   tie-averaged ranks, or 0 when either row is constant.
+ * Both comparisons are made on the fp32 values as given.  recall, rho fp32
+ * [B,H,n] (out).  Supported: 1 <= keep <= n <= 512. */
+int ba_att_rank_agreement(int32_t B, int32_t H, int32_t n_blocks, int32_t keep, const float* x,
+                          const float* r, float* recall, float* rho, void* stream);
+
 /* Static description of a status code. */
 const char* ba_att_status_string(int status);
 

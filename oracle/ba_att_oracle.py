@@ -82,6 +82,7 @@ __all__ = [
     "select_head",
     "select_oracle",
     "postdownsample_map",
+    "postdownsample_map_rows",
     "block_attention",
     "block_attention_rows",
     "dense_attention",
@@ -371,6 +372,29 @@ def postdownsample_map(q: np.ndarray, k: np.ndarray, b: int, scale: float):
             m = blk.max()
             M_lme[I, J] = m + math.log(np.exp(blk - m).mean())
             M_prob[I, J] = P[rs, cs].mean()
+    return M_lme, M_prob
+
+
+def postdownsample_map_rows(q: np.ndarray, k: np.ndarray, b: int, scale: float, blocks):
+    """Rows `blocks` (query-block indices) of both maps of postdownsample_map,
+    from the logits of those blocks' queries only: X_I = scale * q_I k^T,
+    row-softmax normalised over all N keys, pooled per key block."""
+    N = q.shape[0]
+    n = num_blocks(N, b)
+    M_lme = np.empty((len(blocks), n))
+    M_prob = np.empty((len(blocks), n))
+    for a, I in enumerate(blocks):
+        rs = slice(I * b, min((I + 1) * b, N))
+        X = scale * (q[rs] @ k.T)
+        rowmax = X.max(axis=1, keepdims=True)
+        E = np.exp(X - rowmax)
+        P = E / E.sum(axis=1, keepdims=True)
+        for J in range(n):
+            cs = slice(J * b, min((J + 1) * b, N))
+            blk = X[:, cs]
+            m = blk.max()
+            M_lme[a, J] = m + math.log(np.exp(blk - m).mean())
+            M_prob[a, J] = P[:, cs].mean()
     return M_lme, M_prob
 
 

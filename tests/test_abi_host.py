@@ -184,3 +184,41 @@ def test_python_binding_fails_loudly_without_library(tmp_path):
             _lib.load(str(tmp_path / "missing.so"))
     finally:
         _lib._lib = saved
+
+
+def test_diagnostics_reject_before_launch(lib):
+    kf = 128 + 128 * 129
+    ws = lib.ba_att_score_full_workspace_bytes(1, 32, 8192, 128, 64)
+    assert ws >= 2 * 32 * 128 * kf * 4 and ws % 4 == 0
+    assert lib.ba_att_score_full_workspace_bytes(1, 1, 1024, 96, 64) == 0
+    assert lib.ba_att_score_full_workspace_bytes(1, 1, 1024, 64, 32) == 0
+    assert lib.ba_att_score_full_workspace_bytes(1, 1, 64 * 513, 64, 64) == 0  # n > 512
+
+    def bmap(**kw):
+        a = dict(B=1, H=1, N=1024, D=64, block=64, q=FAKE, k=FAKE, lse=FAKE, ml=FAKE, mp=FAKE)
+        a.update(kw)
+        return lib.ba_att_block_map(a["B"], a["H"], a["N"], a["D"], a["block"], 0.0, a["q"], a["k"], a["lse"],
+                                    a["ml"], a["mp"], None)
+
+    assert bmap(q=None) == 1 and bmap(ml=None) == 1
+    assert bmap(lse=None) == 1 and bmap(mp=None) == 1  # lse and m_prob go together
+    assert bmap(D=96) == 2 and bmap(block=256) == 2 and bmap(q=FAKE + 2) == 1
+    assert bmap(N=64 * 2049) == 2  # LDS partials of more than 4096 (block, wave) pairs
+
+    def full(**kw):
+        a = dict(B=1, H=1, N=1024, D=64, block=64, q=FAKE, k=FAKE, sf=FAKE, sm=None, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.ba_att_score_full(a["B"], a["H"], a["N"], a["D"], a["block"], 0.0, a["q"], a["k"], a["sf"],
+                                     a["sm"], a["ws"], a["wsb"], None)
+
+    assert full(sf=None) == 1 and full(k=None) == 1 and full(D=80) == 2 and full(block=16) == 2
+    assert full(ws=None) == 3 and full(wsb=4096) == 3 and full(ws=FAKE + 4) == 3
+
+    def agree(**kw):
+        a = dict(B=1, H=1, n=16, keep=8, x=FAKE, r=FAKE, rec=FAKE, rho=FAKE)
+        a.update(kw)
+        return lib.ba_att_rank_agreement(a["B"], a["H"], a["n"], a["keep"], a["x"], a["r"], a["rec"], a["rho"],
+                                         None)
+
+    assert agree(keep=0) == 1 and agree(keep=17) == 1 and agree(x=None) == 1 and agree(rho=None) == 1
+    assert agree(n=513, keep=8) == 2 and agree(x=FAKE + 2) == 1

@@ -619,3 +619,14 @@ def test_planted_ordinal_ranks_fail_the_library_pin(monkeypatch):
     r = np.round(x + rng.normal(size=40), 0)
     _, rho = orc.rank_agreement(x, r, 10)
     assert abs(rho - scipy.stats.spearmanr(x, r).statistic) > 1e-3
+
+
+def test_postdownsample_map_rows_are_rows_of_the_map():
+    rng = np.random.default_rng(26)
+    N, b, D, scale = 150, 32, 6, 0.5
+    q, k = rng.normal(size=(N, D)), rng.normal(size=(N, D))
+    M_lme, M_prob = orc.postdownsample_map(q, k, b, scale)
+    rows = [4, 0, 2]
+    R_lme, R_prob = orc.postdownsample_map_rows(q, k, b, scale, rows)
+    assert np.allclose(R_lme, M_lme[rows], rtol=0, atol=1e-13)
+    assert np.allclose(R_prob, M_prob[rows], rtol=0, atol=1e-15)
