@@ -9,8 +9,11 @@ sparsity, Q/K/V ~ N(0,1) with 2% planted salient keys).
 Prints ONE JSON line: dense-equivalent attention TFLOP/s of the step
 (4*B*H*N^2*D per step / step time), the speedup over this library's own
 dense kernel, a roofline object for the dominant kernel (the sparse
-attention kernel, bf16 MFMA), one for the selection pass (HBM), and the fp64
-CPU oracle timed on a bounded sample of the same workload.
+attention kernel, bf16 MFMA), one for the selection pass (HBM), the split
+key-list measurement, the selection-quality report (recall / rank
+correlation of the block scores against the exact post-downsample map; not
+part of the timed step), and the fp64 CPU oracle timed on a bounded sample
+of the same workload.
 """
 
 from __future__ import annotations
@@ -58,6 +61,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
     ap.add_argument("--skip-split", action="store_true", help="omit the split key-list measurement")
+    ap.add_argument("--skip-quality", action="store_true",
+                    help="omit the selection-quality report (block recall / rank correlation)")
     return ap.parse_args()
 
 
@@ -302,6 +307,12 @@ def main():
         split_kv = split_kv_measurement(lib, dev, stream, args.warmup, max(5, args.steps // 2))
         print(f"[bench] split key lists: {split_kv}", file=sys.stderr, flush=True)
 
+    quality = None
+    if not args.skip_quality:
+        from block_sparse_attention_ba_amd import quality as qmod
+        quality = qmod.measure(q, k, v, blk, sp)
+        print(f"[bench] selection quality: {quality}", file=sys.stderr, flush=True)
+
     # ---- HBM traffic from the committed counter runs, if they match these kernels
     traffic = None
     src_hash = kernel_source_hash()
@@ -350,6 +361,7 @@ def main():
                             "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,
                             "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
         "split_kv": split_kv,
+        "selection_quality": quality,
         "kernel_source_hash": src_hash,
     }
     if not args.skip_cpu:
