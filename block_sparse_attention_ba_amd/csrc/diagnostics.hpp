@@ -282,8 +282,8 @@ __global__ __launch_bounds__(256) void moments_kernel(const uint16_t* __restrict
     const int r = slot / CPR, s = slot % CPR;
     voff[j] = r * ROW_BYTES + v_slot<CPR>(r, s) * 16;
   }
-  // (the resource goes straight into the copies: a named local of the
-  // resource type in a kernel template drops its host launch stub)
+  // (through dma_tile: the buffer-to-LDS builtin called from a kernel
+  // template's body makes the host pass drop the kernel's launch stub)
   dma_tile<DMA, WAVES>(make_rsrc(src, rows * ROW_BYTES), X, wave, voff);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
