@@ -63,16 +63,8 @@ struct AttnParams {
 };
 
 constexpr int kChunk = 64;  // keys per LDS chunk
-#ifndef BA_RESCALE_SLACK
-#define BA_RESCALE_SLACK 0.0f
-#endif
-// log2 headroom before the running max moves.  0 keeps the exact running max,
-// so the largest probability of a row is exactly 1 before bf16 rounding; a
-// positive slack skips more rescales but rounds that probability too.
-constexpr float kRescaleSlack = BA_RESCALE_SLACK;
 
 #define BA_LDS __attribute__((address_space(3)))
-#define BA_GLOBAL __attribute__((address_space(1)))
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte slot of logical chunk c in row r of a K tile / a V tile
@@ -293,7 +285,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     }
     float mloc = fmaxf(fmaxf(ma, sacc[0][15]), fmaxf(mb, sacc[1][15]));
     mloc = pair_max(mloc) * sl2;
-    if (__any(mloc > m_run + kRescaleSlack)) {
+    if (__any(mloc > m_run)) {  // exact running max: a row's largest probability is 1
       const float m_new = fmaxf(m_run, mloc);
       if (m_new != -__builtin_inff()) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
