@@ -365,6 +365,9 @@ def main():
                             "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
         "split_kv": split_kv,
         "selection_quality": quality,
+        # the pages' only operator-speed figure, as context: it names no hardware,
+        # sequence length or sparsity, so it is no target for this measurement
+        "paper_context": "up to 6.95x over FlashAttention (hardware, shape and sparsity not stated)",
         "kernel_source_hash": src_hash,
     }
     if not args.skip_cpu:
