@@ -16,7 +16,7 @@ namespace {
 
 constexpr int kMaxN = 1 << 20;
 constexpr int kMaxBlocksPerRow = 1024;  // mask -> index rows
-constexpr int kMaxSelectBlocks = 512;   // score rows staged in LDS: 16 rows x n fp32
+constexpr int kMaxSelectBlocks = ba::kMaxScoreBlocks;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

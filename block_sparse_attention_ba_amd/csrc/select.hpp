@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restr
 // over order-preserving uint32 keys and writes mask, ascending idx and cnt.
 // ---------------------------------------------------------------------------
 constexpr int kScoreRows = 16;
+constexpr int kMaxScoreBlocks = 512;  // longest row: 16 rows x n fp32 scores staged in LDS
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = __lane_id();
@@ -265,7 +266,9 @@ __device__ __forceinline__ void radix_select_row(const uint32_t (&key)[NI], int 
   if (lane == 0) *cnt_out = base;
 }
 
-constexpr int kScoreWaves = 8;
+constexpr int kScoreWaves = 16;
+constexpr int kScoreColWaves = 8;  // waves per half of the dot products
+constexpr int kMaxColRounds = (kMaxScoreBlocks + 16 * kScoreColWaves - 1) / (16 * kScoreColWaves);
 
 template <int D, int NI>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const float* __restrict__ aq,
@@ -275,7 +278,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
                                                          int32_t* __restrict__ cnt,
                                                          float* __restrict__ score, int total) {
   constexpr int K3 = 3 * D;
-  constexpr int KM = K3 / 16;        // float4 operand loads per 16x16 tile
+  constexpr int KH = K3 / 2;         // each wave takes one half of the 3D-long dot products
+  constexpr int KM = KH / 16;        // float4 operand loads per 16x16 tile and half
   constexpr int R = kScoreRows;
   constexpr int AP = K3 + 4;         // padded LDS row pitch of the A tile (floats)
   __shared__ __attribute__((aligned(16))) float Atile[R * AP];
@@ -290,6 +294,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
+  const int half = wave & 1;               // which half of k this wave sums
+  const int cw = wave >> 1;                // column-tile lane of the wave: tiles cw, cw + 8, ...
 
   // stage the 16 query-block rows of aq once (coalesced float4)
   for (int e = threadIdx.x; e < R * (K3 / 4); e += kScoreWaves * 64) {
@@ -302,35 +308,59 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
   const int ctiles = (n + 15) / 16;
   auto load_b = [&](int ct, f32x4 (&bfr)[KM]) {
     const int col = ct * 16 + li;
-    const float* Bp = ak + ((size_t)bh * n + col) * K3 + 4 * lg;
+    const float* Bp = ak + ((size_t)bh * n + col) * K3 + half * KH + 4 * lg;
 #pragma unroll
     for (int m = 0; m < KM; ++m)
       bfr[m] = col < n ? *reinterpret_cast<const f32x4*>(Bp + 16 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   f32x4 bfr[KM];
-  if (wave < ctiles) load_b(wave, bfr);  // in flight while the A tile is staged
+  if (cw < ctiles) load_b(cw, bfr);  // in flight while the A tile is staged
   __syncthreads();
-  for (int ct = wave; ct < ctiles; ct += kScoreWaves) {
-    if (ct != wave) load_b(ct, bfr);
+  // first half: straight into Sbuf; second half: kept in registers, added
+  // after a barrier (a fixed order, so the sum is deterministic)
+  f32x4 acc2[kMaxColRounds];
+#pragma unroll
+  for (int t = 0; t < kMaxColRounds; ++t) {
+    const int ct = cw + kScoreColWaves * t;
+    acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ct >= ctiles) continue;
+    if (t > 0) load_b(ct, bfr);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(Atile + li * AP + 16 * m + 4 * lg);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(Atile + li * AP + half * KH + 16 * m + 4 * lg);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bfr[m][e], acc, 0, 0, 0);
     }
     // lane holds column ct*16 + li of rows 4*lg + r
     const int col = ct * 16 + li;
-    if (col < n) {
+    if (half == 0) {
+      if (col < n) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * lg + r;
-        Sbuf[row * n + col] = acc[r];
-        if (score != nullptr && R0 + row < n) score[((size_t)bh * n + R0 + row) * n + col] = acc[r];
+        for (int r = 0; r < 4; ++r) Sbuf[(4 * lg + r) * n + col] = acc[r];
+      }
+    } else {
+      acc2[t] = acc;
+    }
+  }
+  __syncthreads();
+  if (half == 1) {
+#pragma unroll
+    for (int t = 0; t < kMaxColRounds; ++t) {
+      const int col = (cw + kScoreColWaves * t) * 16 + li;
+      if (col < n) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sbuf[(4 * lg + r) * n + col] += acc2[t][r];
       }
     }
   }
   __syncthreads();
+  if (score != nullptr) {  // the score map as the selection saw it, row by row
+    for (int e = threadIdx.x; e < R * n; e += kScoreWaves * 64) {
+      const int row = e / n, col = e - row * n;
+      if (R0 + row < n) score[((size_t)bh * n + R0 + row) * n + col] = Sbuf[e];
+    }
+  }
 
   for (int r = wave; r < R; r += kScoreWaves) {
     const int I = R0 + r;
