@@ -144,9 +144,14 @@ def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
     t0 = time.perf_counter()
     with threadpool_limits(limits=cores):
         blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        t_sel = t_att = 0.0
         for bh in heads:
+            a = time.perf_counter()
             sel = orc.select_oracle(x["q"], x["k"], w.block, sp, heads=[bh])
+            b = time.perf_counter()
             orc.attention_oracle(x["q"], x["k"], x["v"], sel["mask"], w.block, heads=[bh])
+            t_sel += b - a
+            t_att += time.perf_counter() - b
             done += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -162,7 +167,7 @@ def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
     except OSError:
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle",
+            "kind": "oracle", "select_s": round(t_sel, 3), "attention_s": round(t_att, 3),
             "sample": f"{done} of {len(heads)} heads of the same workload (selection + "
                       f"block-sparse attention, fp64 numpy), {dt:.1f} s on {model or 'host CPU'}; "
                       "dense-equivalent FLOPs of the sampled heads / wall time"}
@@ -260,8 +265,10 @@ def main():
         e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sel_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    spa_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    sel_t = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    spa_t = np.array([b.elapsed_time(c) for _, b, c in ev])
+    sel_ms, spa_ms = float(sel_t.mean()), float(spa_t.mean())
+    pct = lambda t: [round(float(np.percentile(t, 10)), 5), round(float(np.percentile(t, 90)), 5)]
     step_ms = wall * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {step_ms:.4f} ms/step (select {sel_ms:.4f} ms, "
           f"sparse attention {spa_ms:.4f} ms)", file=sys.stderr, flush=True)
@@ -284,7 +291,8 @@ def main():
         if i >= args.warmup:
             sel_flushed.append((a, b))
     torch.cuda.synchronize()
-    sel_flush_ms = float(np.median([a.elapsed_time(b) for a, b in sel_flushed]))
+    sel_flush_t = np.array([a.elapsed_time(b) for a, b in sel_flushed])
+    sel_flush_ms = float(np.median(sel_flush_t))
     del flush, sink
     sel_bytes = 2.0 * B * H * N * D * 2 + B * H * n * n + 4.0 * B * H * n * keep + 4.0 * B * H * n
 
@@ -355,6 +363,7 @@ def main():
         "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "select_ms": round(sel_ms, 5),
         "sparse_attention_ms": round(spa_ms, 5),
+        "p10_p90_ms": {"select": pct(sel_t), "sparse_attention": pct(spa_t), "select_flushed": pct(sel_flush_t)},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel (sparse)",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
