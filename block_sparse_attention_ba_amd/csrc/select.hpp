@@ -142,13 +142,15 @@ __global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restr
 
 // ---------------------------------------------------------------------------
 // Compact score and norm sort.  One workgroup per (b*h, 16 query-block
-// rows, 8 waves).  S = aq . ak^T is a small fp32 GEMM (K = 3D) done with
-// v_mfma_f32_16x16x4_f32: each wave owns 16x16 output tiles; operands are
-// loaded from L2 as float4 (lane group g = l/16 takes k = 16m + 4g + e for
-// MFMA step (m, e), the same assignment for both operands, so the product is
-// unchanged).  The S rows are staged in LDS; then one wave per row selects
-// the `keep` largest scores (ties to lower J) by an MSB-first radix select
-// over order-preserving uint32 keys and writes mask, ascending idx and cnt.
+// rows, 16 waves).  S = aq . ak^T is a small fp32 GEMM (K = 3D) done with
+// v_mfma_f32_16x16x4_f32: wave w sums half (w % 2) of the dot products for
+// the 16x16 output tiles w/2, w/2 + 8, ...; operands are loaded from L2 as
+// float4 (lane group g = l/16 takes k = 16m + 4g + e for MFMA step (m, e),
+// the same assignment for both operands, so the product is unchanged).  The
+// first halves are written to LDS and the second halves added after a
+// barrier; then one wave per row selects the `keep` largest scores (ties to
+// lower J) by an MSB-first radix select over order-preserving uint32 keys and
+// writes mask, ascending idx and cnt.
 // ---------------------------------------------------------------------------
 constexpr int kScoreRows = 16;
 constexpr int kMaxScoreBlocks = 512;  // longest row: 16 rows x n fp32 scores staged in LDS
