@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
     ap.add_argument("--skip-split", action="store_true", help="omit the split key-list measurement")
+    ap.add_argument("--skip-sweep", action="store_true",
+                    help="omit the long-context sweep (16K tokens, block 64/128, sparsity 0/50/75%%)")
     ap.add_argument("--skip-quality", action="store_true",
                     help="omit the selection-quality report (block recall / rank correlation)")
     return ap.parse_args()
@@ -120,6 +122,64 @@ def split_kv_measurement(lib, dev, stream, warmup: int, reps: int) -> dict:
     res["best_split"] = int(best[0])
     res["speedup"] = round(res["unsplit_ms"] / best[1], 3)
     return res
+
+
+def long_context_sweep(dev, stream, warmup: int, reps: int) -> list:
+    """The long-context workloads (B1 H32 N16384 D128, block 64 and 128) at each
+    of their sparsities: select + sparse step time against the dense kernel,
+    all on resident inputs.  Times are means of HIP-event pairs on the stream
+    after `warmup` untimed repetitions."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_ba_amd import api, workloads
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # the two long-context workloads share their inputs; only the block differs
+    x = workloads.make_inputs("long_b64")
+    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
+    del x
+    out = []
+    for name in ("long_b64", "long_b128"):
+        w = workloads.WORKLOADS[name]
+        B, H, N, D, blk = w.B, w.H, w.N, w.D, w.block
+        assert tuple(q.shape) == (B, H, N, D)
+        o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in evs:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+        dense_ms = timed(lambda: api.dense(q, k, v, out_dtype=torch.bfloat16, out=o, lse=lse))
+        dense_flops = 4.0 * B * H * N * N * D
+        ws = torch.empty(api.select_workspace_bytes(B, H, N, D, blk), dtype=torch.uint8, device=dev)
+        for sp in w.sparsities:
+            mask, idx, cnt = api.select(q, k, blk, sp, workspace=ws)
+
+            def step():
+                _, i2, c2 = api.select(q, k, blk, sp, workspace=ws)
+                api.forward(q, k, v, i2, c2, blk, out_dtype=torch.bfloat16, out=o, lse=lse)
+
+            step_ms = timed(step)
+            kept = kept_tile_flops(mask.cpu().numpy(), N, D, blk)
+            out.append({"workload": name, "shape": f"B{B} H{H} N{N} D{D} b{blk}", "sparsity": sp,
+                        "keep": int(idx.shape[-1]), "step_ms": round(step_ms, 5), "dense_ms": round(dense_ms, 5),
+                        "speedup_vs_dense": round(dense_ms / step_ms, 4),
+                        "dense_equiv_tflops": round(dense_flops / step_ms / 1e9, 1),
+                        "kept_tile_tflops": round(kept / step_ms / 1e9, 1)})
+        del o, lse, ws
+    del q, k, v
+    torch.cuda.empty_cache()
+    return out
 
 
 def kept_tile_flops(mask, N: int, D: int, block: int) -> float:
@@ -318,6 +378,11 @@ def main():
         split_kv = split_kv_measurement(lib, dev, stream, args.warmup, max(5, args.steps // 2))
         print(f"[bench] split key lists: {split_kv}", file=sys.stderr, flush=True)
 
+    sweep = None
+    if not args.skip_sweep:
+        sweep = long_context_sweep(dev, stream, 5, 10)
+        print(f"[bench] long-context sweep: {sweep}", file=sys.stderr, flush=True)
+
     quality = None
     if not args.skip_quality:
         from block_sparse_attention_ba_amd import quality as qmod
@@ -373,6 +438,7 @@ def main():
                             "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,
                             "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
         "split_kv": split_kv,
+        "long_context_sweep": sweep,
         "selection_quality": quality,
         # the pages' only operator-speed figure, as context: it names no hardware,
         # sequence length or sparsity, so it is no target for this measurement
