@@ -630,3 +630,27 @@ def test_postdownsample_map_rows_are_rows_of_the_map():
     R_lme, R_prob = orc.postdownsample_map_rows(q, k, b, scale, rows)
     assert np.allclose(R_lme, M_lme[rows], rtol=0, atol=1e-13)
     assert np.allclose(R_prob, M_prob[rows], rtol=0, atol=1e-15)
+
+
+def test_oracle_matches_its_stored_golden_results():
+    """Regression fixture of the oracle itself (tests/golden/oracle_tiny.json,
+    written by tests/golden/make_oracle_golden.py from the oracle alone: the
+    pages print no worked example)."""
+    import json
+    import os
+    import sys
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    sys.path.insert(0, here)
+    try:
+        import make_oracle_golden as mk
+    finally:
+        sys.path.remove(here)
+    with open(os.path.join(here, "oracle_tiny.json")) as f:
+        gold = json.load(f)
+    now = mk.compute()
+    assert now["keep"] == gold["keep"]
+    assert now["mask"] == gold["mask"] and now["idx"] == gold["idx"]
+    assert np.allclose(now["S"], gold["S"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(now["lse"], gold["lse"], rtol=1e-12, atol=1e-12)
+    for r, row in gold["o_rows"].items():
+        assert np.allclose(now["o_rows"][r], row, rtol=1e-11, atol=1e-12), r
