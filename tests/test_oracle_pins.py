@@ -654,3 +654,33 @@ def test_oracle_matches_its_stored_golden_results():
     assert np.allclose(now["lse"], gold["lse"], rtol=1e-12, atol=1e-12)
     for r, row in gold["o_rows"].items():
         assert np.allclose(now["o_rows"][r], row, rtol=1e-11, atol=1e-12), r
+
+
+def test_p7_gaussian_log_mgf():
+    """Q block-constant, K ~ N(km, diag sigma^2): the block log-mean-exp is the
+    log-MGF of a Gaussian, scale<q,km> + scale^2/2 sum q^2 sigma^2, which is
+    exactly the q^2*vk term of the corrected score (the other two vanish)."""
+    import scipy.special
+    scale = 0.5
+    qv = np.array([0.8, -0.5, 1.2, 0.3])
+    km = np.array([0.3, 0.9, -0.4, 0.2])
+    sd = np.array([0.5, 0.7, 0.4, 0.9])
+    # for a block-constant query block, M_lme[I, J] = ln mean_{t in J} e^{scale <q, k_t>}
+    rng = np.random.default_rng(27)
+    ks = km + sd * rng.standard_normal((64, 4))
+    qs = np.tile(qv, (64, 1))
+    M, _ = orc.postdownsample_map(np.vstack([qs]), np.vstack([ks]), 64, scale)
+    assert abs(M[0, 0] - (scipy.special.logsumexp(scale * ks @ qv) - math.log(64))) < 1e-13
+    # large key block: S (sample statistics) against the brute-force map and the closed form
+    J = 200_000
+    k = km + sd * rng.standard_normal((J, 4))
+    brute = scipy.special.logsumexp(scale * k @ qv) - math.log(J)
+    qm, qvar = orc.block_stats(np.tile(qv, (8, 1)), 8)
+    kmean, kvar = orc.block_stats(k, J)
+    S = orc.compact_score(qm, qvar, kmean, kvar, scale)[0, 0]
+    closed = scale * qv @ km + 0.5 * scale ** 2 * np.sum(qv ** 2 * sd ** 2)
+    assert abs(S - brute) < 1e-3, (S, brute)
+    assert abs(S - closed) < 3e-3, (S, closed)
+    # a planted missing 1/2 on the correction misses by about scale^2/2 * sum q^2 sd^2 = 0.073
+    wrong = scale * (qm @ kmean.T)[0, 0] + scale ** 2 * np.sum(qm[0] ** 2 * kvar[0])
+    assert abs(wrong - brute) > 0.05
