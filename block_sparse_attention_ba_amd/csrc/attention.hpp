@@ -315,6 +315,13 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
       }
     }
     l_run += psum;
+    // Four-wave tiles: keep the softmax ahead of the wait for V(c) so that it
+    // covers the copy (without the fence the compiler sinks it past the
+    // barrier, next to its use in O^T += V^T P^T).  Two-wave tiles are faster
+    // with the sunk form, where the exponentials fill the gaps between the
+    // PV MFMAs and the copy of K(c+1) starts earlier.
+    if constexpr (WAVES == 4)
+      __asm__ volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l_run));
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(c) landed
     __syncthreads();  // V(c) visible; every wave is done with K(c)
