@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline")
     ap.add_argument("--skip-dense", action="store_true", help="omit the dense comparator")
+    ap.add_argument("--skip-flushed", action="store_true",
+                    help="omit the step and dense timings with L2 and the MALL flushed before each repetition")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
@@ -353,7 +355,6 @@ def main():
     torch.cuda.synchronize()
     sel_flush_t = np.array([a.elapsed_time(b) for a, b in sel_flushed])
     sel_flush_ms = float(np.median(sel_flush_t))
-    del flush, sink
     sel_bytes = 2.0 * B * H * N * D * 2 + B * H * n * n + 4.0 * B * H * n * keep + 4.0 * B * H * n
 
     # ---- the dense comparator
@@ -372,6 +373,43 @@ def main():
         dense_ms = float(np.mean([a.elapsed_time(b) for a, b in evd]))
         print(f"[bench] dense {dense_ms:.4f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s)",
               file=sys.stderr, flush=True)
+
+    # ---- the step and the dense comparator again, each repetition after the
+    # same 1 GiB flushing read (no input left in L2 or the MALL)
+    flushed = None
+    if not args.skip_flushed and not args.skip_dense:
+        reps = max(10, args.steps // 2)
+        ev_step, ev_dense = [], []
+        for _ in range(reps):
+            torch.sum(flush, dim=0, out=sink)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            select()
+            e[1].record(stream)
+            sparse()
+            e[2].record(stream)
+            ev_step.append(e)
+        for _ in range(reps):
+            torch.sum(flush, dim=0, out=sink)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            dense()
+            e[1].record(stream)
+            ev_dense.append(e)
+        torch.cuda.synchronize()
+        f_sel = np.array([e[0].elapsed_time(e[1]) for e in ev_step])
+        f_spa = np.array([e[1].elapsed_time(e[2]) for e in ev_step])
+        f_step = np.array([e[0].elapsed_time(e[2]) for e in ev_step])
+        f_dense = np.array([e[0].elapsed_time(e[1]) for e in ev_dense])
+        fs, fd = float(np.median(f_step)), float(np.median(f_dense))
+        flushed = {"reps": reps, "flush": "1 GiB read before each repetition",
+                   "step_ms": round(fs, 5), "select_ms": round(float(np.median(f_sel)), 5),
+                   "sparse_attention_ms": round(float(np.median(f_spa)), 5), "dense_ms": round(fd, 5),
+                   "speedup_vs_dense": round(fd / fs, 4),
+                   "dense_equiv_tflops": round(dense_flops / (fs * 1e-3) / 1e12, 2),
+                   "p10_p90_ms": {"step": pct(f_step), "dense": pct(f_dense)}}
+        print(f"[bench] flushed: {flushed}", file=sys.stderr, flush=True)
+    del flush, sink
 
     split_kv = None
     if not args.skip_split:
@@ -437,6 +475,7 @@ def main():
                             "achieved": round(sel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,
                             "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
+        "flushed": flushed,
         "split_kv": split_kv,
         "long_context_sweep": sweep,
         "selection_quality": quality,
