@@ -36,17 +36,35 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None) -> None:
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype | None, ndim: int | None = None,
+          device: torch.device | None = None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
-    if t.dtype != dtype:
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
+    if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def _on(t: torch.Tensor):
+    """The library launches on the current device: make it the arguments' device."""
+    return torch.cuda.device(t.device)
+
+
+def _workspace(ws: torch.Tensor | None, need: int, device: torch.device) -> tuple[torch.Tensor, int]:
+    """A caller's workspace (any dtype, contiguous, on the arguments' device) or a new one;
+    returns it with its size in bytes."""
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    else:
+        _need(ws, "workspace", None, device=device)
+    return ws, ws.numel() * ws.element_size()
 
 
 def num_blocks(N: int, block: int) -> int:
@@ -71,7 +89,7 @@ def select(q: torch.Tensor, k: torch.Tensor, block: int, sparsity: float, scale:
     """Selection pass: returns (mask uint8 [B,H,n,n], idx int32 [B,H,n,keep],
     cnt int32 [B,H,n]) and, with return_score, the fp32 score map."""
     B, H, N, D = _qkv_shape(q)
-    _need(k, "k", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4, q.device)
     if tuple(k.shape) != (B, H, N, D):
         raise ValueError("q and k must have the same shape")
     lib = _lib.load()
@@ -84,14 +102,12 @@ def select(q: torch.Tensor, k: torch.Tensor, block: int, sparsity: float, scale:
     idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, H, n), dtype=torch.int32, device=dev)
     score = torch.empty((B, H, n, n), dtype=torch.float32, device=dev) if return_score else None
-    need = select_workspace_bytes(B, H, N, D, block)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _check(lib.ba_att_select(B, H, N, D, block, float(scale or 0.0), float(sparsity),
-                             q.data_ptr(), k.data_ptr(), mask.data_ptr(), idx.data_ptr(),
-                             cnt.data_ptr(), score.data_ptr() if score is not None else None,
-                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             _stream(q)))
+    workspace, ws_bytes = _workspace(workspace, select_workspace_bytes(B, H, N, D, block), dev)
+    with _on(q):
+        _check(lib.ba_att_select(B, H, N, D, block, float(scale or 0.0), float(sparsity),
+                                 q.data_ptr(), k.data_ptr(), mask.data_ptr(), idx.data_ptr(),
+                                 cnt.data_ptr(), score.data_ptr() if score is not None else None,
+                                 workspace.data_ptr(), ws_bytes, _stream(q)))
     if return_score:
         return mask, idx, cnt, score
     return mask, idx, cnt
@@ -106,8 +122,9 @@ def mask_to_index(mask: torch.Tensor, max_keep: int | None = None):
     max_keep = n if max_keep is None else int(max_keep)
     idx = torch.empty((B, H, n, max_keep), dtype=torch.int32, device=mask.device)
     cnt = torch.empty((B, H, n), dtype=torch.int32, device=mask.device)
-    _check(_lib.load().ba_att_mask_to_index(B, H, n, mask.data_ptr(), max_keep, idx.data_ptr(),
-                                            cnt.data_ptr(), _stream(mask)))
+    with _on(mask):
+        _check(_lib.load().ba_att_mask_to_index(B, H, n, mask.data_ptr(), max_keep, idx.data_ptr(),
+                                                cnt.data_ptr(), _stream(mask)))
     return idx, cnt
 
 
@@ -118,13 +135,15 @@ def _out(q, out_dtype, out, lse, return_lse):
     if out is None:
         out = torch.empty((B, H, N, D), dtype=out_dtype, device=q.device)
     else:
-        _need(out, "out", out_dtype, 4)
+        _need(out, "out", out_dtype, 4, q.device)
         if tuple(out.shape) != tuple(q.shape):
             raise ValueError("out must have the shape of q")
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if lse is not None:
-        _need(lse, "lse", torch.float32, 3)
+        _need(lse, "lse", torch.float32, 3, q.device)
+        if tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be [B,H,N]")
     code = BA_F32 if out_dtype == torch.float32 else BA_BF16
     return out, lse, code
 
@@ -132,32 +151,24 @@ def _out(q, out_dtype, out, lse, return_lse):
 def forward(q, k, v, idx, cnt, block: int, scale: float | None = None,
             out_dtype: torch.dtype = torch.float32, out=None, lse=None, return_lse: bool = True):
     """Block-sparse attention over the listed key blocks; returns (O, LSE)."""
-    B, H, N, D = _qkv_shape(q)
-    for name, t in (("k", k), ("v", v)):
-        _need(t, name, torch.bfloat16, 4)
-        if tuple(t.shape) != (B, H, N, D):
-            raise ValueError(f"{name} must have the shape of q")
-    _need(idx, "idx", torch.int32, 4)
-    _need(cnt, "cnt", torch.int32, 3)
-    n = num_blocks(N, block)
-    if tuple(idx.shape[:3]) != (B, H, n) or tuple(cnt.shape) != (B, H, n):
-        raise ValueError("idx/cnt must be [B,H,n,max_keep] / [B,H,n]")
+    B, H, N, D = _forward_args(q, k, v, idx, cnt, block)
     out, lse, code = _out(q, out_dtype, out, lse, return_lse)
-    _check(_lib.load().ba_att_forward(B, H, N, D, block, float(scale or 0.0), q.data_ptr(),
-                                      k.data_ptr(), v.data_ptr(), idx.data_ptr(), cnt.data_ptr(),
-                                      int(idx.shape[3]), out.data_ptr(), code,
-                                      lse.data_ptr() if lse is not None else None, _stream(q)))
+    with _on(q):
+        _check(_lib.load().ba_att_forward(B, H, N, D, block, float(scale or 0.0), q.data_ptr(),
+                                          k.data_ptr(), v.data_ptr(), idx.data_ptr(), cnt.data_ptr(),
+                                          int(idx.shape[3]), out.data_ptr(), code,
+                                          lse.data_ptr() if lse is not None else None, _stream(q)))
     return out, lse
 
 
 def _forward_args(q, k, v, idx, cnt, block):
     B, H, N, D = _qkv_shape(q)
     for name, t in (("k", k), ("v", v)):
-        _need(t, name, torch.bfloat16, 4)
+        _need(t, name, torch.bfloat16, 4, q.device)
         if tuple(t.shape) != (B, H, N, D):
             raise ValueError(f"{name} must have the shape of q")
-    _need(idx, "idx", torch.int32, 4)
-    _need(cnt, "cnt", torch.int32, 3)
+    _need(idx, "idx", torch.int32, 4, q.device)
+    _need(cnt, "cnt", torch.int32, 3, q.device)
     n = num_blocks(N, block)
     if tuple(idx.shape[:3]) != (B, H, n) or tuple(cnt.shape) != (B, H, n):
         raise ValueError("idx/cnt must be [B,H,n,max_keep] / [B,H,n]")
@@ -178,13 +189,12 @@ def forward_split(q, k, v, idx, cnt, block: int, n_split: int, scale: float | No
     need = forward_split_workspace_bytes(B, H, N, D, n_split)
     if need == 0:
         raise ValueError("n_split must lie in [1, 64]")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(_lib.load().ba_att_forward_split(
-        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
-        cnt.data_ptr(), int(idx.shape[3]), int(n_split), out.data_ptr(), code,
-        lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(q)))
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    with _on(q):
+        _check(_lib.load().ba_att_forward_split(
+            B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+            cnt.data_ptr(), int(idx.shape[3]), int(n_split), out.data_ptr(), code,
+            lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_bytes, _stream(q)))
     return out, lse
 
 
@@ -193,19 +203,15 @@ def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.dtype
     """Exact log-space merge of attention results over disjoint key sets:
     o_parts fp32 [P,B,H,N,D], lse_parts fp32 [P,B,H,N] -> (O, LSE)."""
     _need(o_parts, "o_parts", torch.float32, 5)
-    _need(lse_parts, "lse_parts", torch.float32, 4)
+    _need(lse_parts, "lse_parts", torch.float32, 4, o_parts.device)
     P, B, H, N, D = (int(x) for x in o_parts.shape)
     if tuple(lse_parts.shape) != (P, B, H, N):
         raise ValueError("lse_parts must be [P,B,H,N]")
-    if out_dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
-    if out is None:
-        out = torch.empty((B, H, N, D), dtype=out_dtype, device=o_parts.device)
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
-    code = BA_F32 if out_dtype == torch.float32 else BA_BF16
-    _check(_lib.load().ba_att_merge(B, H, N, D, P, o_parts.data_ptr(), lse_parts.data_ptr(), out.data_ptr(),
-                                    code, lse.data_ptr() if lse is not None else None, _stream(o_parts)))
+    out, lse, code = _out(o_parts[0], out_dtype, out, lse, return_lse)
+    with _on(o_parts):
+        _check(_lib.load().ba_att_merge(B, H, N, D, P, o_parts.data_ptr(), lse_parts.data_ptr(),
+                                        out.data_ptr(), code, lse.data_ptr() if lse is not None else None,
+                                        _stream(o_parts)))
     return out, lse
 
 
@@ -215,15 +221,16 @@ def forward_ext(q, k, v, idx, cnt, block: int, o_ext: torch.Tensor, lse_ext: tor
     """Block-sparse attention merged with an external attention result
     (o_ext fp32 [B,H,N,D], lse_ext fp32 [B,H,N]) over a disjoint key set."""
     B, H, N, D = _forward_args(q, k, v, idx, cnt, block)
-    _need(o_ext, "o_ext", torch.float32, 4)
-    _need(lse_ext, "lse_ext", torch.float32, 3)
+    _need(o_ext, "o_ext", torch.float32, 4, q.device)
+    _need(lse_ext, "lse_ext", torch.float32, 3, q.device)
     if tuple(o_ext.shape) != (B, H, N, D) or tuple(lse_ext.shape) != (B, H, N):
         raise ValueError("o_ext/lse_ext must be [B,H,N,D] / [B,H,N]")
     out, lse, code = _out(q, out_dtype, out, lse, return_lse)
-    _check(_lib.load().ba_att_forward_ext(
-        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
-        cnt.data_ptr(), int(idx.shape[3]), o_ext.data_ptr(), lse_ext.data_ptr(), out.data_ptr(), code,
-        lse.data_ptr() if lse is not None else None, _stream(q)))
+    with _on(q):
+        _check(_lib.load().ba_att_forward_ext(
+            B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+            cnt.data_ptr(), int(idx.shape[3]), o_ext.data_ptr(), lse_ext.data_ptr(), out.data_ptr(), code,
+            lse.data_ptr() if lse is not None else None, _stream(q)))
     return out, lse
 
 
@@ -232,13 +239,14 @@ def dense(q, k, v, scale: float | None = None, out_dtype: torch.dtype = torch.fl
     """Dense attention softmax(scale Q K^T) V; returns (O, LSE)."""
     B, H, N, D = _qkv_shape(q)
     for name, t in (("k", k), ("v", v)):
-        _need(t, name, torch.bfloat16, 4)
+        _need(t, name, torch.bfloat16, 4, q.device)
         if tuple(t.shape) != (B, H, N, D):
             raise ValueError(f"{name} must have the shape of q")
     out, lse, code = _out(q, out_dtype, out, lse, return_lse)
-    _check(_lib.load().ba_att_dense(B, H, N, D, float(scale or 0.0), q.data_ptr(), k.data_ptr(),
-                                    v.data_ptr(), out.data_ptr(), code,
-                                    lse.data_ptr() if lse is not None else None, _stream(q)))
+    with _on(q):
+        _check(_lib.load().ba_att_dense(B, H, N, D, float(scale or 0.0), q.data_ptr(), k.data_ptr(),
+                                        v.data_ptr(), out.data_ptr(), code,
+                                        lse.data_ptr() if lse is not None else None, _stream(q)))
     return out, lse
 
 
@@ -256,20 +264,21 @@ def block_map(q, k, block: int, lse: torch.Tensor | None = None, scale: float | 
     over all keys (fp32 [B,H,N], e.g. from dense), M_prob fp32 [B,H,n,n]
     (block mean of the softmax probabilities); M_prob is None without lse."""
     B, H, N, D = _qkv_shape(q)
-    _need(k, "k", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4, q.device)
     if tuple(k.shape) != (B, H, N, D):
         raise ValueError("k must have the shape of q")
     if lse is not None:
-        _need(lse, "lse", torch.float32, 3)
+        _need(lse, "lse", torch.float32, 3, q.device)
         if tuple(lse.shape) != (B, H, N):
             raise ValueError("lse must be [B,H,N]")
     n = num_blocks(N, block)
     m_lme = torch.empty((B, H, n, n), dtype=torch.float32, device=q.device)
     m_prob = torch.empty_like(m_lme) if lse is not None else None
-    _check(_lib.load().ba_att_block_map(
-        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(),
-        lse.data_ptr() if lse is not None else None, m_lme.data_ptr(),
-        m_prob.data_ptr() if m_prob is not None else None, _stream(q)))
+    with _on(q):
+        _check(_lib.load().ba_att_block_map(
+            B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(),
+            lse.data_ptr() if lse is not None else None, m_lme.data_ptr(),
+            m_prob.data_ptr() if m_prob is not None else None, _stream(q)))
     return m_lme, m_prob
 
 
@@ -281,20 +290,20 @@ def score_full(q, k, block: int, scale: float | None = None, workspace: torch.Te
     """Block scores with full block covariances and without any correction:
     returns (S_full, S_mean), fp32 [B,H,n,n] each."""
     B, H, N, D = _qkv_shape(q)
-    _need(k, "k", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4, q.device)
     if tuple(k.shape) != (B, H, N, D):
         raise ValueError("k must have the shape of q")
     n = num_blocks(N, block)
     need = score_full_workspace_bytes(B, H, N, D, block)
     if need == 0:
         raise RuntimeError("BA-Att call failed: unsupported shape for the full-covariance score")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     s_full = torch.empty((B, H, n, n), dtype=torch.float32, device=q.device)
     s_mean = torch.empty_like(s_full)
-    _check(_lib.load().ba_att_score_full(
-        B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), s_full.data_ptr(),
-        s_mean.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
+    with _on(q):
+        _check(_lib.load().ba_att_score_full(
+            B, H, N, D, block, float(scale or 0.0), q.data_ptr(), k.data_ptr(), s_full.data_ptr(),
+            s_mean.data_ptr(), workspace.data_ptr(), ws_bytes, _stream(q)))
     return s_full, s_mean
 
 
@@ -302,14 +311,15 @@ def rank_agreement(x: torch.Tensor, r: torch.Tensor, keep: int):
     """Per row of two block maps fp32 [B,H,n,n]: (recall, rho) fp32 [B,H,n] --
     overlap of the kept sets (norm-sort rule) / keep, and Spearman's rho."""
     _need(x, "x", torch.float32, 4)
-    _need(r, "r", torch.float32, 4)
+    _need(r, "r", torch.float32, 4, x.device)
     if x.shape != r.shape or x.shape[2] != x.shape[3]:
         raise ValueError("x and r must be the same [B,H,n,n] shape")
     B, H, n, _ = (int(v) for v in x.shape)
     recall = torch.empty((B, H, n), dtype=torch.float32, device=x.device)
     rho = torch.empty_like(recall)
-    _check(_lib.load().ba_att_rank_agreement(B, H, n, int(keep), x.data_ptr(), r.data_ptr(),
-                                             recall.data_ptr(), rho.data_ptr(), _stream(x)))
+    with _on(x):
+        _check(_lib.load().ba_att_rank_agreement(B, H, n, int(keep), x.data_ptr(), r.data_ptr(),
+                                                 recall.data_ptr(), rho.data_ptr(), _stream(x)))
     return recall, rho
 
 

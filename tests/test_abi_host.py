@@ -222,3 +222,13 @@ def test_diagnostics_reject_before_launch(lib):
 
     assert agree(keep=0) == 1 and agree(keep=17) == 1 and agree(x=None) == 1 and agree(rho=None) == 1
     assert agree(n=513, keep=8) == 2 and agree(x=FAKE + 2) == 1
+
+
+def test_python_binding_rejects_host_tensors_before_any_call():
+    import torch
+    from block_sparse_attention_ba_amd import api
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.dense(x, x, x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.select(x, x, 64, 0.5)
