@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline")
     ap.add_argument("--skip-dense", action="store_true", help="omit the dense comparator")
+    ap.add_argument("--skip-peaks", action="store_true",
+                    help="omit the machine-peak microbenchmarks (HBM read/copy, bf16 MFMA)")
     ap.add_argument("--skip-flushed", action="store_true",
                     help="omit the step and dense timings with L2 and the MALL flushed before each repetition")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -233,6 +235,59 @@ def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
             "sample": f"{done} of {len(heads)} heads of the same workload (selection + "
                       f"block-sparse attention, fp64 numpy), {dt:.1f} s on {model or 'host CPU'}; "
                       "dense-equivalent FLOPs of the sampled heads / wall time"}
+
+
+def measured_peaks(dev, stream, reps: int = 5) -> dict:
+    """HBM read and copy bandwidth and the bf16 MFMA rate measured on this GPU
+    (libba_peaks.so), as context for the vendor peaks the rooflines use."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_ba_amd import _lib
+    pk = _lib.load_peaks()
+    sptr = stream.cuda_stream
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(f):
+        if f() != 0:
+            raise RuntimeError("peak microbenchmark launch failed")
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            f()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    # the best over a few grid sizes (2 workgroups per CU reads fastest: each
+    # grid-stride round then covers a compact 2 MB span)
+    grids = [2, 8, 32]
+    sink = torch.empty(n_cu * max(grids) * 256, dtype=torch.int32, device=dev)
+    nbytes = 4 << 30  # far beyond the 256 MB MALL: every byte comes from HBM
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    half = nbytes // 2
+    t_read = {g: timed(lambda: pk.ba_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), n_cu * g, sptr))
+              for g in grids}
+    t_copy = {g: timed(lambda: pk.ba_peak_copy(buf.data_ptr(), buf.data_ptr() + half, half, n_cu * g, sptr))
+              for g in grids}
+    del buf, sink
+    g_read, g_copy = min(t_read, key=t_read.get), min(t_copy, key=t_copy.get)
+    mwg, iters = n_cu * 2, 20000  # two waves per SIMD, four independent MFMA chains each
+    fsink = torch.empty(mwg * 256, dtype=torch.float32, device=dev)
+    t_mfma = timed(lambda: pk.ba_peak_mfma_bf16(fsink.data_ptr(), mwg, iters, 2.0 ** -10, sptr))
+    del fsink
+    mfma_tfs = mwg * 4 * iters * 4 * 32768 / t_mfma / 1e12
+    return {
+        "hbm_read_tbs": round(nbytes / t_read[g_read] / 1e12, 3),
+        "hbm_copy_tbs": round(2 * half / t_copy[g_copy] / 1e12, 3),
+        "workgroups_per_cu": {"read": g_read, "copy": g_copy},
+        "mfma_bf16_tflops": round(mfma_tfs, 1),
+        # v_mfma_f32_32x32x16_bf16: 32768 FLOP per 32 cycles per SIMD, 4 SIMDs per CU
+        "implied_clock_ghz": round(mfma_tfs * 1e12 / (n_cu * 4 * 1024) / 1e9, 3),
+        "vendor": {"hbm_tbs": HBM_PEAK_GBS / 1000.0, "mfma_bf16_tflops": MFMA_BF16_PEAK_TFS},
+        "workload": "read 4 GiB and copy 2 GiB (best of 2/8/32 workgroups per CU); "
+                    "2 waves per SIMD x 20000 rounds of 4 independent MFMAs",
+    }
 
 
 def main():
@@ -421,6 +476,11 @@ def main():
         sweep = long_context_sweep(dev, stream, 5, 10)
         print(f"[bench] long-context sweep: {sweep}", file=sys.stderr, flush=True)
 
+    peaks = None
+    if not args.skip_peaks:
+        peaks = measured_peaks(dev, stream)
+        print(f"[bench] measured peaks: {peaks}", file=sys.stderr, flush=True)
+
     quality = None
     if not args.skip_quality:
         from block_sparse_attention_ba_amd import quality as qmod
@@ -476,6 +536,7 @@ def main():
                             "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,
                             "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
         "flushed": flushed,
+        "measured_peaks": peaks,
         "split_kv": split_kv,
         "long_context_sweep": sweep,
         "selection_quality": quality,

@@ -56,3 +56,33 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+# ---- libba_peaks.so: machine-peak microbenchmarks (include/ba_peaks.h), for
+# the rooflines' context only
+PEAKS_PATH = os.path.join(_PKG, "libba_peaks.so")
+PEAK_SIGNATURES = [
+    ("ba_peak_read", ctypes.c_int, [_p, _sz, _p, _i32, _p]),
+    ("ba_peak_copy", ctypes.c_int, [_p, _p, _sz, _i32, _p]),
+    ("ba_peak_mfma_bf16", ctypes.c_int, [_p, _i32, _i32, _f32, _p]),
+]
+
+_peaks = None
+
+
+def load_peaks(path: str | None = None) -> ctypes.CDLL:
+    """Loads the built microbenchmark library once; raises if it is missing."""
+    global _peaks
+    if _peaks is not None:
+        return _peaks
+    path = path or PEAKS_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"peak microbenchmark library not found at {path}; build it with "
+                          "`python -m block_sparse_attention_ba_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, res, args in PEAK_SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _peaks = lib
+    return lib

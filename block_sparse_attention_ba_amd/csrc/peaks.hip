@@ -1,0 +1,92 @@
+// Machine-peak microbenchmarks (include/ba_peaks.h): streaming HBM read,
+// HBM copy and the bf16 matrix-core rate, measured on the GPU the library
+// runs on, as context for the vendor peaks its rooflines are priced against.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ba_peaks.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src, size_t n,
+                                                        uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  // four loads in flight per thread per round
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n; i += stride) acc ^= src[i];
+  sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        size_t n) {
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_kernel(float* __restrict__ sink, int iters, float x) {
+  const __bf16 v = (__bf16)x;
+  const bf16x8 a = {v, v, v, v, v, v, v, v};
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int finish() { return hipGetLastError() == hipSuccess ? 0 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int ba_peak_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !aligned16(src) || workgroups < 1) return 1;
+  read_kernel<<<dim3((unsigned)workgroups), kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(src), bytes / 16, sink);
+  return finish();
+}
+
+int ba_peak_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, void* stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst) || workgroups < 1)
+    return 1;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  if (s < d + bytes && d < s + bytes) return 1;  // overlapping
+  copy_kernel<<<dim3((unsigned)workgroups), kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  return finish();
+}
+
+int ba_peak_mfma_bf16(float* sink, int32_t workgroups, int32_t iters, float x, void* stream) {
+  if (!sink || workgroups < 1 || iters < 1) return 1;
+  mfma_kernel<<<dim3((unsigned)workgroups), kThreads, 0, static_cast<hipStream_t>(stream)>>>(sink, iters, x);
+  return finish();
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+/* Machine-peak microbenchmarks for the rooflines of libba_att.
+ *
+ * Not part of the attention operator: three kernels that confirm, on the GPU
+ * the library runs on, the two constants its rooflines are priced against --
+ * HBM bandwidth (streaming read, and copy) and the bf16 matrix-core rate --
+ * next to the vendor's figures.  Built into libba_peaks.so.
+ *
+ * Conventions as in ba_att.h: device pointers, a hipStream_t passed as void*,
+ * the caller owns every buffer, nothing is allocated, arguments are checked
+ * before any launch (0 = ok, 1 = invalid argument, 4 = HIP launch error).
+ */
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads `bytes` bytes at src once (16-byte vector loads, grid-stride over
+ * `workgroups` workgroups of 256 threads) and writes one 32-bit XOR digest
+ * per thread to sink[workgroups*256], so that no load can be dropped.
+ * src 16-byte aligned, bytes a positive multiple of 16. */
+int ba_peak_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
+/* Copies `bytes` bytes from src to dst (16-byte vectors, grid-stride).
+ * Both 16-byte aligned and not overlapping; bytes a positive multiple of 16. */
+int ba_peak_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, void* stream);
+
+/* Every wave of `workgroups` workgroups (4 waves each) issues `iters` rounds of
+ * four independent v_mfma_f32_32x32x16_bf16 on register operands (2*32*32*16
+ * FLOP each, no memory traffic in the loop); operands are x in bf16.  Each
+ * thread writes the sum of its accumulators to sink[workgroups*256].
+ * FLOPs = workgroups * 4 * iters * 4 * 32768. */
+int ba_peak_mfma_bf16(float* sink, int32_t workgroups, int32_t iters, float x, void* stream);
+
+#ifdef __cplusplus
+}
+#endif

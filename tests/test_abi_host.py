@@ -232,3 +232,25 @@ def test_python_binding_rejects_host_tensors_before_any_call():
         api.dense(x, x, x)
     with pytest.raises(ValueError, match="GPU tensor"):
         api.select(x, x, 64, 0.5)
+
+
+def test_peaks_library_exports_its_header_and_rejects_bad_arguments():
+    import ctypes
+    from block_sparse_attention_ba_amd import _lib
+    if not os.path.exists(_lib.PEAKS_PATH):
+        from block_sparse_attention_ba_amd import build
+        build.build()
+    peaks = _lib.load_peaks()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ba_peaks.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(ba_peak_\w+)\s*\(", text)))
+    assert declared == sorted(name for name, _, _ in _lib.PEAK_SIGNATURES)
+    for name in declared:
+        assert hasattr(peaks, name), name
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below is rejected on the host
+    assert peaks.ba_peak_read(None, 16, fake, 1, None) == 1
+    assert peaks.ba_peak_read(fake, 15, fake, 1, None) == 1
+    assert peaks.ba_peak_read(fake, 16, fake, 0, None) == 1
+    assert peaks.ba_peak_copy(fake, fake, 64, 1, None) == 1  # overlapping
+    assert peaks.ba_peak_copy(ctypes.c_void_p((1 << 20) + 8), ctypes.c_void_p(1 << 30), 64, 1, None) == 1
+    assert peaks.ba_peak_mfma_bf16(None, 1, 1, 0.0, None) == 1
+    assert peaks.ba_peak_mfma_bf16(fake, 1, 0, 0.0, None) == 1
