@@ -254,3 +254,51 @@ def test_custom_scale_and_end_to_end_tiny(gpu_lib):
     Oo, Lo = orc.attention_oracle(x["q"], x["k"], x["v"], mask.cpu().numpy(), 64, scale=scale)[(0, 0)]
     assert max_abs(o.cpu().numpy()[0, 0], Oo) <= O_TOL
     assert max_abs(lse.cpu().numpy()[0, 0], Lo) <= LSE_TOL
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_forward_list_contract_edge_cases(gpu_lib, block):
+    """The index-list contract of ba_att_forward (include/ba_att.h): a count
+    above max_keep is clamped, a negative count is an empty row, entries
+    outside [0, n) are skipped wherever they stand, any order is accepted,
+    and a repeated entry is counted twice.  Each row is checked against
+    textbook attention over exactly the multiset of keys its list names."""
+    import torch
+    B, H, N, D = 1, 1, 1000, 64
+    q, k, v = make_case(B, H, N, D, "clustered", seed=123)
+    n = orc.num_blocks(N, block)
+    max_keep = 6
+    rng = np.random.default_rng(block)
+    idx = np.full((B, H, n, max_keep), -1, np.int32)
+    cnt = np.zeros((B, H, n), np.int32)
+    lists = {}
+    for I in range(n):
+        picks = rng.choice(n, size=min(4, n), replace=False)
+        lists[I] = list(picks)
+    lists[0] = [n - 1, 0, 2][: min(3, n)]           # descending-first order, tail block included
+    lists[1] = [1, -1, n + 3, 0][: 4]                # invalid entries in the middle
+    lists[2] = [2, 2, 0] if n > 2 else [0, 0]        # a repeated entry
+    for I, lst in lists.items():
+        idx[0, 0, I, :len(lst)] = lst
+        cnt[0, 0, I] = len(lst)
+    cnt[0, 0, n - 1] = max_keep + 5                  # clamped to max_keep
+    idx[0, 0, n - 1] = rng.permutation(n)[:max_keep] if n >= max_keep else np.resize(np.arange(n), max_keep)
+    if n > 3:
+        cnt[0, 0, 3] = -3                            # empty row
+    o, lse = gpu_lib.forward(to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(idx).cuda(),
+                             torch.from_numpy(cnt).cuda(), block)
+    torch.cuda.synchronize()
+    o, lse = o[0, 0].cpu().numpy(), lse[0, 0].cpu().numpy()
+    qq, kk, vv = (orc.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
+    scale = 1.0 / math.sqrt(D)
+    for I in range(n):
+        rows = np.arange(I * block, min((I + 1) * block, N))
+        c = min(max(int(cnt[0, 0, I]), 0), max_keep)
+        keys = [t for J in idx[0, 0, I, :c] if 0 <= J < n for t in range(J * block, min((J + 1) * block, N))]
+        if not keys:
+            assert np.all(o[rows] == 0) and np.all(np.isneginf(lse[rows])), I
+            continue
+        keys = np.asarray(keys)
+        Oe, Le = orc.dense_attention(qq[rows], kk[keys], vv[keys], scale)
+        assert max_abs(o[rows], Oe) <= O_TOL, I
+        assert max_abs(lse[rows], Le) <= LSE_TOL, I
