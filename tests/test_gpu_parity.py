@@ -54,6 +54,7 @@ SELECT_CASES = [
     (1, 2, 8192, 128, 64, 0.9, "clustered"),    # 128 blocks per row
     (1, 1, 16384, 64, 64, 0.5, "normal"),       # 256 blocks per row
     (1, 1, 20000, 128, 64, 0.5, "clustered"),   # 313 blocks: 5 elements per lane
+    (1, 2, 1024, 128, 64, 0.95, "clustered"),   # keep = 1 of 16: the row maximum alone
 ]
 
 
