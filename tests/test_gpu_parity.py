@@ -262,8 +262,9 @@ def test_forward_list_contract_edge_cases(gpu_lib, block):
     """The index-list contract of ba_att_forward (include/ba_att.h): a count
     above max_keep is clamped, a negative count is an empty row, entries
     outside [0, n) are skipped wherever they stand, any order is accepted,
-    and a repeated entry is counted twice.  Each row is checked against
-    textbook attention over exactly the multiset of keys its list names."""
+    and a repeated entry is counted twice -- also when the lists are cut into
+    parts (ba_att_forward_split).  Each row is checked against textbook
+    attention over exactly the multiset of keys its list names."""
     import torch
     B, H, N, D = 1, 1, 1000, 64
     q, k, v = make_case(B, H, N, D, "clustered", seed=123)
@@ -286,20 +287,21 @@ def test_forward_list_contract_edge_cases(gpu_lib, block):
     idx[0, 0, n - 1] = rng.permutation(n)[:max_keep] if n >= max_keep else np.resize(np.arange(n), max_keep)
     if n > 3:
         cnt[0, 0, 3] = -3                            # empty row
-    o, lse = gpu_lib.forward(to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(idx).cuda(),
-                             torch.from_numpy(cnt).cuda(), block)
+    args = (to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), block)
+    results = {"forward": gpu_lib.forward(*args), "forward_split(3)": gpu_lib.forward_split(*args, 3)}
     torch.cuda.synchronize()
-    o, lse = o[0, 0].cpu().numpy(), lse[0, 0].cpu().numpy()
     qq, kk, vv = (orc.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
     scale = 1.0 / math.sqrt(D)
-    for I in range(n):
-        rows = np.arange(I * block, min((I + 1) * block, N))
-        c = min(max(int(cnt[0, 0, I]), 0), max_keep)
-        keys = [t for J in idx[0, 0, I, :c] if 0 <= J < n for t in range(J * block, min((J + 1) * block, N))]
-        if not keys:
-            assert np.all(o[rows] == 0) and np.all(np.isneginf(lse[rows])), I
-            continue
-        keys = np.asarray(keys)
-        Oe, Le = orc.dense_attention(qq[rows], kk[keys], vv[keys], scale)
-        assert max_abs(o[rows], Oe) <= O_TOL, I
-        assert max_abs(lse[rows], Le) <= LSE_TOL, I
+    for path, (o, lse) in results.items():
+        o, lse = o[0, 0].cpu().numpy(), lse[0, 0].cpu().numpy()
+        for I in range(n):
+            rows = np.arange(I * block, min((I + 1) * block, N))
+            c = min(max(int(cnt[0, 0, I]), 0), max_keep)
+            keys = [t for J in idx[0, 0, I, :c] if 0 <= J < n for t in range(J * block, min((J + 1) * block, N))]
+            if not keys:
+                assert np.all(o[rows] == 0) and np.all(np.isneginf(lse[rows])), (path, I)
+                continue
+            keys = np.asarray(keys)
+            Oe, Le = orc.dense_attention(qq[rows], kk[keys], vv[keys], scale)
+            assert max_abs(o[rows], Oe) <= O_TOL, (path, I)
+            assert max_abs(lse[rows], Le) <= LSE_TOL, (path, I)
