@@ -6,7 +6,7 @@
 
 #include "ba_peaks.h"
 
-namespace {
+namespace ba {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -58,6 +58,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(float* __restrict__ sink
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+}  // namespace ba
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int finish() { return hipGetLastError() == hipSuccess ? 0 : 4; }
@@ -68,8 +72,8 @@ extern "C" {
 
 int ba_peak_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
   if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !aligned16(src) || workgroups < 1) return 1;
-  read_kernel<<<dim3((unsigned)workgroups), kThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const u32x4*>(src), bytes / 16, sink);
+  ba::read_kernel<<<dim3((unsigned)workgroups), ba::kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const ba::u32x4*>(src), bytes / 16, sink);
   return finish();
 }
 
@@ -78,14 +82,14 @@ int ba_peak_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, v
     return 1;
   const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
   if (s < d + bytes && d < s + bytes) return 1;  // overlapping
-  copy_kernel<<<dim3((unsigned)workgroups), kThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  ba::copy_kernel<<<dim3((unsigned)workgroups), ba::kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const ba::u32x4*>(src), static_cast<ba::u32x4*>(dst), bytes / 16);
   return finish();
 }
 
 int ba_peak_mfma_bf16(float* sink, int32_t workgroups, int32_t iters, float x, void* stream) {
   if (!sink || workgroups < 1 || iters < 1) return 1;
-  mfma_kernel<<<dim3((unsigned)workgroups), kThreads, 0, static_cast<hipStream_t>(stream)>>>(sink, iters, x);
+  ba::mfma_kernel<<<dim3((unsigned)workgroups), ba::kThreads, 0, static_cast<hipStream_t>(stream)>>>(sink, iters, x);
   return finish();
 }
 
