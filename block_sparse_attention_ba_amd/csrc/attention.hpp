@@ -20,14 +20,15 @@
 //  * Keys are processed in chunks of 64.  K and V chunks are copied HBM/L2 ->
 //    LDS by direct-to-LDS buffer loads (no register staging; loads past the
 //    sequence end return zero) into one K and one V buffer used in
-//    ping-pong: V(c) streams in while S^T(c) and the softmax run, K(c+1)
-//    streams in while O^T += V(c) P^T runs.  16-byte chunks of every row are
+//    ping-pong: V(c) streams in while S^T(c) and the row maxima are formed
+//    (and, in four-wave tiles, the whole softmax), K(c+1) streams in while
+//    O^T += V(c) P^T runs.  16-byte chunks of every row are
 //    XOR-swizzled so that both the row reads of K and the transposing reads
 //    of V are free of bank conflicts.  MFMA operands are read from LDS one
 //    step ahead of their use.
-//  * Online softmax in the log2 domain, fp32.  The accumulators of a wave are
-//    rescaled only in chunks where some query's running max grows (a
-//    wave-uniform branch), which becomes rare once the maxima settle.
+//  * Online softmax in the log2 domain, fp32, with the exact running max.  The
+//    accumulators of a wave are rescaled only in chunks where some query of
+//    the wave finds a new maximum (a wave-uniform branch).
 //  * The sparse variant walks the compacted block-index list of its query
 //    block; the dense variant walks all keys.  Keys >= N are masked to -inf.
 #pragma once
