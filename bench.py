@@ -125,6 +125,8 @@ def split_kv_measurement(lib, dev, stream, warmup: int, reps: int) -> dict:
     res["unsplit_ms"] = round(res["unsplit_ms"], 5)
     res["best_split"] = int(best[0])
     res["speedup"] = round(res["unsplit_ms"] / best[1], 3)
+    # the library's own choice for this shape (ba_att_forward_split_parts)
+    res["suggested_split"] = int(lib.ba_att_forward_split_parts(B, H, N, blk, keep))
     return res
 
 

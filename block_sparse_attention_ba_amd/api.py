@@ -17,7 +17,8 @@ BA_BF16, BA_F32 = 0, 1
 
 __all__ = [
     "load", "num_blocks", "keep_count", "select_workspace_bytes", "select", "mask_to_index",
-    "forward", "forward_split", "forward_split_workspace_bytes", "merge", "forward_ext", "dense",
+    "forward", "forward_split", "forward_split_workspace_bytes", "forward_split_parts", "forward_auto",
+    "merge", "forward_ext", "dense",
     "ba_attention", "block_map", "score_full_workspace_bytes", "score_full", "rank_agreement",
 ]
 
@@ -196,6 +197,26 @@ def forward_split(q, k, v, idx, cnt, block: int, n_split: int, scale: float | No
             cnt.data_ptr(), int(idx.shape[3]), int(n_split), out.data_ptr(), code,
             lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_bytes, _stream(q)))
     return out, lse
+
+
+def forward_split_parts(B: int, H: int, N: int, block: int, max_keep: int) -> int:
+    """n_split that fills the current device once (1: no split needed)."""
+    parts = int(_lib.load().ba_att_forward_split_parts(B, H, N, block, max_keep))
+    if parts < 1:
+        raise ValueError("invalid shape, or the device cannot be queried")
+    return parts
+
+
+def forward_auto(q, k, v, idx, cnt, block: int, scale: float | None = None,
+                 out_dtype: torch.dtype = torch.float32, out=None, lse=None, return_lse: bool = True):
+    """ba_att_forward, or ba_att_forward_split with the suggested number of
+    parts when the unsplit launch would leave the device partly idle."""
+    B, H, N, D = _forward_args(q, k, v, idx, cnt, block)
+    with _on(q):
+        parts = forward_split_parts(B, H, N, block, int(idx.shape[3]))
+    if parts == 1:
+        return forward(q, k, v, idx, cnt, block, scale, out_dtype, out, lse, return_lse)
+    return forward_split(q, k, v, idx, cnt, block, parts, scale, out_dtype, out, lse, return_lse)
 
 
 def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.dtype = torch.float32,

@@ -4,6 +4,8 @@
 // enqueues kernels on the caller's stream.  Nothing is allocated and nothing
 // synchronises the host.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -262,6 +264,21 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
 size_t ba_att_forward_split_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t n_split) {
   if (check_shape(B, H, N, D) != BA_OK || n_split < 1 || n_split > kMaxSplit) return 0;
   return (size_t)n_split * B * H * N * (size_t)(D + 1) * sizeof(float);
+}
+
+int32_t ba_att_forward_split_parts(int32_t B, int32_t H, int32_t N, int32_t block, int32_t max_keep) {
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN || max_keep < 1 || (block != 64 && block != 128)) return 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+  // resident attention workgroups per compute unit: the two-wave tile (block
+  // 64) holds 2 waves per SIMD, the four-wave tile (block 128) 3
+  const long long resident = (long long)cus * (block == 64 ? 4 : 3);
+  const long long tiles = (long long)B * H * num_blocks(N, block);
+  long long parts = resident / tiles;  // the largest count that still fits one round
+  parts = std::min(parts, (long long)max_keep * (block / ba::kChunk));
+  parts = std::min(parts, (long long)kMaxSplit);
+  return (int32_t)std::max(parts, 1ll);
 }
 
 int ba_att_forward_split(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,

@@ -254,3 +254,11 @@ def test_peaks_library_exports_its_header_and_rejects_bad_arguments():
     assert peaks.ba_peak_copy(ctypes.c_void_p((1 << 20) + 8), ctypes.c_void_p(1 << 30), 64, 1, None) == 1
     assert peaks.ba_peak_mfma_bf16(None, 1, 1, 0.0, None) == 1
     assert peaks.ba_peak_mfma_bf16(fake, 1, 0, 0.0, None) == 1
+
+
+def test_split_parts_rejects_invalid_shapes_before_any_device_query(lib):
+    assert lib.ba_att_forward_split_parts(0, 1, 1024, 64, 4) == 0
+    assert lib.ba_att_forward_split_parts(1, 1, 0, 64, 4) == 0
+    assert lib.ba_att_forward_split_parts(1, 1, 1024, 96, 4) == 0
+    assert lib.ba_att_forward_split_parts(1, 1, 1024, 64, 0) == 0
+    assert lib.ba_att_forward_split_parts(1, 1, (1 << 20) + 1, 64, 4) == 0

@@ -156,3 +156,29 @@ def test_forward_ext_empty_external_is_plain_forward(gpu_lib):
     o1, l1 = gpu_lib.forward(Q, K, V, idx, cnt, block)
     torch.cuda.synchronize()
     assert torch.equal(o, o1) and torch.equal(lse, l1)
+
+
+def test_suggested_split_fills_the_device_once(gpu_lib):
+    """ba_att_forward_split_parts: the largest part count whose workgroups
+    fit one round of this GPU, and forward_auto equal to the unsplit forward
+    within the split tolerance."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for (B, H, N, block, max_keep) in [(1, 1, 32768, 64, 256), (1, 32, 8192, 64, 64), (1, 1, 8192, 64, 64),
+                                       (1, 1, 8192, 128, 32), (1, 1, 1000, 64, 2), (2, 4, 4096, 128, 16)]:
+        tiles = B * H * orc.num_blocks(N, block)
+        resident = cus * (4 if block == 64 else 3)
+        parts = gpu_lib.forward_split_parts(B, H, N, block, max_keep)
+        assert 1 <= parts <= min(64, max_keep * block // 64)
+        assert parts == 1 or parts * tiles <= resident        # one round
+        assert parts == min(64, max_keep * block // 64) or (parts + 1) * tiles > resident  # the largest such
+    B, H, N, D, block = 1, 2, 3000, 128, 64
+    q, k, v = (to_dev(rand_bits((B, H, N, D), 500 + i)) for i in range(3))
+    mask, idx, cnt = gpu_lib.select(q, k, block, 0.5)
+    assert gpu_lib.forward_split_parts(B, H, N, block, int(idx.shape[3])) > 1
+    o_ref, l_ref = gpu_lib.forward(q, k, v, idx, cnt, block)
+    o, l = gpu_lib.forward_auto(q, k, v, idx, cnt, block)
+    torch.cuda.synchronize()
+    vmax = float(v.float().abs().max())
+    assert float((o - o_ref).abs().max()) <= 2.0 ** -8 * vmax
+    assert float((l - l_ref).abs().max()) <= 1e-5
