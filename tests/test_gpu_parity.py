@@ -305,3 +305,37 @@ def test_forward_list_contract_edge_cases(gpu_lib, block):
             Oe, Le = orc.dense_attention(qq[rows], kk[keys], vv[keys], scale)
             assert max_abs(o[rows], Oe) <= O_TOL, (path, I)
             assert max_abs(lse[rows], Le) <= LSE_TOL, (path, I)
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65])
+@pytest.mark.parametrize("D,block", [(64, 64), (128, 128)])
+def test_degenerate_sequence_lengths(gpu_lib, N, D, block):
+    """Sequences of one token, of less than one block, of exactly one block
+    and of one block plus one token, through selection, forward, split
+    forward and dense, against the oracle."""
+    import torch
+    B, H = 1, 2
+    q, k, v = make_case(B, H, N, D, "normal", seed=N + D)
+    ref = orc.select_oracle(q, k, block, 0.5)
+    mask, idx, cnt = gpu_lib.select(to_dev(q), to_dev(k), block, 0.5)
+    torch.cuda.synchronize()
+    res = compare_masks(mask.cpu().numpy(), ref["S"], ref["mask"], ref["keep"])
+    assert not res["bad"], res["bad"][:5]
+    assert np.all(cnt.cpu().numpy() == ref["keep"])
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    oidx, ocnt = torch.from_numpy(ref["idx"]).cuda(), torch.from_numpy(ref["cnt"]).cuda()
+    o, lse = gpu_lib.forward(Q, K, V, oidx, ocnt, block)
+    os_, ls_ = gpu_lib.forward_split(Q, K, V, oidx, ocnt, block, 3)
+    od, ld = gpu_lib.dense(Q, K, V)
+    torch.cuda.synchronize()
+    att = orc.attention_oracle(q, k, v, ref["mask"], block)
+    scale = 1.0 / math.sqrt(D)
+    for h in range(H):
+        Oo, Lo = att[(0, h)]
+        for name, (go, gl) in {"forward": (o, lse), "split": (os_, ls_)}.items():
+            assert max_abs(go[0, h].cpu().numpy(), Oo) <= O_TOL, (name, h)
+            assert max_abs(gl[0, h].cpu().numpy(), Lo) <= LSE_TOL, (name, h)
+        qq, kk, vv = (orc.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
+        Od, Ldn = orc.dense_attention(qq, kk, vv, scale)
+        assert max_abs(od[0, h].cpu().numpy(), Od) <= O_TOL
+        assert max_abs(ld[0, h].cpu().numpy(), Ldn) <= LSE_TOL
