@@ -67,7 +67,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
-    ap.add_argument("--skip-split", action="store_true", help="omit the split key-list measurement")
+    ap.add_argument("--skip-split", action="store_true",
+                    help="omit the split key-list and external-contribution measurements")
     ap.add_argument("--skip-sweep", action="store_true",
                     help="omit the long-context sweep (16K tokens, block 64/128, sparsity 0/50/75%%)")
     ap.add_argument("--skip-quality", action="store_true",
@@ -127,6 +128,57 @@ def split_kv_measurement(lib, dev, stream, warmup: int, reps: int) -> dict:
     res["speedup"] = round(res["unsplit_ms"] / best[1], 3)
     # the library's own choice for this shape (ba_att_forward_split_parts)
     res["suggested_split"] = int(lib.ba_att_forward_split_parts(B, H, N, blk, keep))
+    return res
+
+
+def external_measurement(lib, stream, dims, tensors, warmup: int, reps: int) -> dict:
+    """ba_att_forward_ext against ba_att_forward on the benchmark's own inputs
+    and block lists.  The external part (fp32 O_ext and LSE_ext over another
+    key set) is read once per row in the epilogue, so its extra time is priced
+    against those bytes: B*H*N*(4*D + 4)."""
+    import numpy as np
+    import torch
+    B, H, N, D, blk, keep, code = dims
+    q, k, v, idx, cnt, o, lse = tensors
+    dev = q.device
+    g = torch.Generator(device=dev).manual_seed(20260520)
+    o_ext = torch.randn((B, H, N, D), generator=g, device=dev, dtype=torch.float32)
+    lse_ext = torch.randn((B, H, N), generator=g, device=dev, dtype=torch.float32) + 5.0
+    sptr = stream.cuda_stream
+
+    def run(ext):
+        if ext:
+            st = lib.ba_att_forward_ext(B, H, N, D, blk, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        idx.data_ptr(), cnt.data_ptr(), keep, o_ext.data_ptr(), lse_ext.data_ptr(),
+                                        o.data_ptr(), code, lse.data_ptr(), sptr)
+        else:
+            st = lib.ba_att_forward(B, H, N, D, blk, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    idx.data_ptr(), cnt.data_ptr(), keep, o.data_ptr(), code, lse.data_ptr(), sptr)
+        if st:
+            raise RuntimeError(lib.ba_att_status_string(st).decode())
+
+    def timed(ext):
+        for _ in range(warmup):
+            run(ext)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            run(ext)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    # alternate the two so that clock drift falls on both
+    plain, ext = [], []
+    for _ in range(3):
+        plain.append(timed(False))
+        ext.append(timed(True))
+    t0, t1 = float(np.median(plain)), float(np.median(ext))
+    extra_bytes = B * H * N * (4 * D + 4)
+    res = {"forward_ms": round(t0, 5), "forward_ext_ms": round(t1, 5), "extra_ms": round(t1 - t0, 5),
+           "extra_bytes": extra_bytes,
+           "extra_gbs": round(extra_bytes / ((t1 - t0) * 1e-3) / 1e9, 1) if t1 > t0 else None}
+    del o_ext, lse_ext
     return res
 
 
@@ -479,10 +531,13 @@ def main():
         print(f"[bench] flushed: {flushed}", file=sys.stderr, flush=True)
     del flush, sink
 
-    split_kv = None
+    split_kv = external = None
     if not args.skip_split:
         split_kv = split_kv_measurement(lib, dev, stream, args.warmup, max(5, args.steps // 2))
         print(f"[bench] split key lists: {split_kv}", file=sys.stderr, flush=True)
+        external = external_measurement(lib, stream, (B, H, N, D, blk, keep, code),
+                                        (q, k, v, idx, cnt, o, lse), 10, max(5, args.steps // 2))
+        print(f"[bench] external contribution: {external}", file=sys.stderr, flush=True)
 
     sweep = None
     if not args.skip_sweep:
@@ -552,6 +607,7 @@ def main():
         "flushed": flushed,
         "measured_peaks": peaks,
         "split_kv": split_kv,
+        "external": external,
         "long_context_sweep": sweep,
         "selection_quality": quality,
         # the pages' only operator-speed figure, as context: it names no hardware,
