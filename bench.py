@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
+    ap.add_argument("--power", action="store_true",
+                    help="also sample socket power and graphics clocks (amd-smi) while the sparse and the "
+                         "dense kernel each run back to back for a few seconds")
     ap.add_argument("--skip-split", action="store_true",
                     help="omit the split key-list and external-contribution measurements")
     ap.add_argument("--skip-sweep", action="store_true",
@@ -289,6 +292,48 @@ def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
             "sample": f"{done} of {len(heads)} heads of the same workload (selection + "
                       f"block-sparse attention, fp64 numpy), {dt:.1f} s on {model or 'host CPU'}; "
                       "dense-equivalent FLOPs of the sampled heads / wall time"}
+
+
+def power_sample(run, stream, seconds: float) -> dict:
+    """Runs `run` back to back for about `seconds` while `amd-smi metric -p -c`
+    is sampled three times from a thread; returns the socket power (W) and the
+    graphics clocks (MHz, one per XCD) it read, with the mean call time."""
+    import re
+    import subprocess
+    import threading
+    import time
+    import torch
+    samples = []
+
+    def sampler():
+        time.sleep(min(1.0, seconds / 4))
+        for _ in range(3):
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                                     timeout=20).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            watts = [float(m) for m in re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)]
+            gfx = []
+            for block in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", out):
+                gfx.append(float(block))
+            samples.append({"socket_w": watts[0] if watts else None, "gfx_mhz": gfx})
+            time.sleep(seconds / 6)
+
+    for _ in range(10):
+        run()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    t0 = time.time()
+    th.start()
+    calls = 0
+    while time.time() - t0 < seconds or th.is_alive():
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+        calls += 10
+    ms = (time.time() - t0) * 1e3 / calls
+    return {"mean_ms_per_call": round(ms, 5), "samples": samples}
 
 
 def measured_peaks(dev, stream, reps: int = 5) -> dict:
@@ -531,6 +576,11 @@ def main():
         print(f"[bench] flushed: {flushed}", file=sys.stderr, flush=True)
     del flush, sink
 
+    power = None
+    if args.power:
+        power = {"sparse": power_sample(sparse, stream, 4.0), "dense": power_sample(dense, stream, 4.0)}
+        print(f"[bench] power: {power}", file=sys.stderr, flush=True)
+
     split_kv = external = None
     if not args.skip_split:
         split_kv = split_kv_measurement(lib, dev, stream, args.warmup, max(5, args.steps // 2))
@@ -608,6 +658,7 @@ def main():
         "measured_peaks": peaks,
         "split_kv": split_kv,
         "external": external,
+        "power": power,
         "long_context_sweep": sweep,
         "selection_quality": quality,
         # the pages' only operator-speed figure, as context: it names no hardware,
