@@ -294,11 +294,20 @@ def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
                       "dense-equivalent FLOPs of the sampled heads / wall time"}
 
 
+def parse_amd_smi_metric(text: str) -> dict:
+    """Socket power (W) and the graphics clock of every XCD (MHz) from the text
+    that `amd-smi metric -p -c` prints: `SOCKET_POWER: <W> W` under POWER and
+    `GFX_<i>:` followed by `CLK: <MHz> MHz` under CLOCK."""
+    import re
+    watts = [float(m) for m in re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)]
+    gfx = [float(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    return {"socket_w": watts[0] if watts else None, "gfx_mhz": gfx}
+
+
 def power_sample(run, stream, seconds: float) -> dict:
     """Runs `run` back to back for about `seconds` while `amd-smi metric -p -c`
     is sampled three times from a thread; returns the socket power (W) and the
     graphics clocks (MHz, one per XCD) it read, with the mean call time."""
-    import re
     import subprocess
     import threading
     import time
@@ -313,11 +322,7 @@ def power_sample(run, stream, seconds: float) -> dict:
                                      timeout=20).stdout
             except (OSError, subprocess.SubprocessError):
                 return
-            watts = [float(m) for m in re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)]
-            gfx = []
-            for block in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", out):
-                gfx.append(float(block))
-            samples.append({"socket_w": watts[0] if watts else None, "gfx_mhz": gfx})
+            samples.append(parse_amd_smi_metric(out))
             time.sleep(seconds / 6)
 
     for _ in range(10):
