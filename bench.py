@@ -3,17 +3,20 @@
 A step is one pass of the whole hot path on one batch of synthetic input:
 the selection pass (pool + corrected score + norm sort) followed by the
 block-sparse attention pass, at the workload's sparsity.  The default
-workload is the LLaDA-8B-shaped layer (B1 H32 N8192 D128, block 64, 50%
-sparsity, Q/K/V ~ N(0,1) with 2% planted salient keys).
+workload is the largest single-GPU configuration, the distribution-shift
+stress (B2 H32 N32768 D128, block 128, 50% sparsity, drifting 16-component
+mixture with a local band and planted needle keys).
 
 Prints ONE JSON line: dense-equivalent attention TFLOP/s of the step
 (4*B*H*N^2*D per step / step time), the speedup over this library's own
 dense kernel, a roofline object for the dominant kernel (the sparse
-attention kernel, bf16 MFMA), one for the selection pass (HBM), the split
-key-list measurement, the selection-quality report (recall / rank
-correlation of the block scores against the exact post-downsample map; not
-part of the timed step), and the fp64 CPU oracle timed on a bounded sample
-of the same workload.
+attention kernel, bf16 MFMA), one for the selection pass (HBM), the same
+step on the LLaDA-8B-shaped layer (and, on request, the video-DiT shape),
+the long-context sweep, the split key-list measurement, the
+selection-quality report (not part of the timed step), the fp64 CPU oracle
+timed on a seeded head subset of the same workload, and the benchmark's
+own outputs checked against that oracle (mask near-tie counts, max |dO|,
+max |dLSE|).
 """
 
 from __future__ import annotations
@@ -33,15 +36,19 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["block_sparse_attention_ba_amd/csrc/attention.hpp",
-                  "block_sparse_attention_ba_amd/csrc/select.hpp",
-                  "block_sparse_attention_ba_amd/csrc/common.hpp",
-                  "block_sparse_attention_ba_amd/csrc/ba_att.hip"]
+# the sources that fix each kernel's memory traffic: a committed counter
+# reading is used only while the hash of its kernel's sources still matches
+KERNEL_SOURCES = {
+    "attention": ["block_sparse_attention_ba_amd/csrc/attention.hpp",
+                  "block_sparse_attention_ba_amd/csrc/common.hpp"],
+    "select": ["block_sparse_attention_ba_amd/csrc/select.hpp",
+               "block_sparse_attention_ba_amd/csrc/common.hpp"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -55,7 +62,7 @@ def parse():
     # sparse step measures ~640 us for its first 25-50 launches, then ~580 us),
     # so the default warm-up covers the ramp and the timed steps see steady state
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="llada8b")
+    ap.add_argument("--workload", default="shift")
     ap.add_argument("--sparsity", type=float, default=None)
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline")
@@ -64,7 +71,11 @@ def parse():
                     help="omit the machine-peak microbenchmarks (HBM read/copy, bf16 MFMA)")
     ap.add_argument("--skip-flushed", action="store_true",
                     help="omit the step and dense timings with L2 and the MALL flushed before each repetition")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="heads of the seeded subset the CPU oracle runs (and the O/LSE parity covers)")
+    ap.add_argument("--extra", default="llada8b",
+                    help="comma-separated further workloads timed as a step against dense "
+                         "(llada8b, video, long_b64, long_b128, tiny; empty for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
     ap.add_argument("--power", action="store_true",
@@ -252,46 +263,99 @@ def kept_tile_flops(mask, N: int, D: int, block: int) -> float:
     return float(4.0 * D * np.einsum("bij,i,j->", m, sizes, sizes))
 
 
-def cpu_baseline(x, w, sp: float, budget_s: float) -> dict:
-    """The fp64 oracle as it stands, timed on this host: selection plus
-    block-sparse attention head by head until the time budget is used."""
-    import numpy as np
-    from threadpoolctl import threadpool_info, threadpool_limits
-    from oracle import ba_att_oracle as orc
-
-    cores = min(16, len(os.sched_getaffinity(0)))
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=cores):
-        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-        t_sel = t_att = 0.0
-        for bh in heads:
-            a = time.perf_counter()
-            sel = orc.select_oracle(x["q"], x["k"], w.block, sp, heads=[bh])
-            b = time.perf_counter()
-            orc.attention_oracle(x["q"], x["k"], x["v"], sel["mask"], w.block, heads=[bh])
-            t_sel += b - a
-            t_att += time.perf_counter() - b
-            done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.N * w.N * w.D * done
-    model = ""
+def cpu_model() -> str:
+    """The host CPU's full model string (/proc/cpuinfo)."""
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle", "select_s": round(t_sel, 3), "attention_s": round(t_att, 3),
-            "sample": f"{done} of {len(heads)} heads of the same workload (selection + "
-                      f"block-sparse attention, fp64 numpy), {dt:.1f} s on {model or 'host CPU'}; "
-                      "dense-equivalent FLOPs of the sampled heads / wall time"}
+    return "unknown host CPU"
+
+
+def sample_heads(name: str, B: int, H: int, count: int) -> list:
+    """A seeded subset of `count` (batch, head) pairs that holds the first and
+    the last head (every head when count >= B*H)."""
+    import zlib
+    import numpy as np
+    every = [(b, h) for b in range(B) for h in range(H)]
+    if count >= len(every):
+        return every
+    rng = np.random.default_rng(zlib.crc32(f"cpu-baseline-{name}".encode()))
+    inner = rng.choice(np.arange(1, len(every) - 1), size=count - 2, replace=False)
+    return [every[i] for i in sorted({0, len(every) - 1, *(int(i) for i in inner)})]
+
+
+def cpu_baseline(x, w, sp: float, heads: list) -> tuple:
+    """The fp64 oracle as it stands, timed on this host: selection plus
+    block-sparse attention of the given heads, one head per host thread
+    (BLAS single-threaded inside each).  Returns the baseline record and the
+    oracle's (mask, O, LSE) per head for the parity check."""
+    from oracle import ba_att_oracle as orc
+    from oracle.parity import host_threads, map_heads
+
+    threads = host_threads()
+    affinity = len(os.sched_getaffinity(0))
+
+    def one(bh):
+        a = time.perf_counter()
+        sel = orc.select_oracle(x["q"], x["k"], w.block, sp, heads=[bh])
+        b = time.perf_counter()
+        O, L = orc.attention_oracle(x["q"], x["k"], x["v"], sel["mask"], w.block, heads=[bh])[bh]
+        return sel["mask"][bh], O, L, b - a, time.perf_counter() - b
+
+    t0 = time.perf_counter()
+    res = map_heads(one, heads, threads)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.N * w.N * w.D * len(heads)
+    record = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(threads, len(heads))),
+              "kind": "oracle", "host_cores_available": affinity, "thread_cap": 16,
+              "cpu_model": cpu_model(), "wall_s": round(dt, 3),
+              "select_s_summed": round(sum(r[3] for r in res), 3),
+              "attention_s_summed": round(sum(r[4] for r in res), 3),
+              "heads": [list(h) for h in heads],
+              "sample": f"{len(heads)} of {w.B * w.H} heads of the same workload (seeded subset with the "
+                        "first and last head; selection + block-sparse attention, fp64 numpy, one head per "
+                        f"thread on {min(threads, len(heads))} threads), {dt:.1f} s; "
+                        "dense-equivalent FLOPs of the sampled heads / wall time"}
+    return record, {h: r[:3] for h, r in zip(heads, res)}
+
+
+def parity_report(x, w, sp: float, gmask, o_own, lse_own, oracle_heads: dict) -> dict:
+    """The benchmark's own outputs against the oracle.
+
+    Masks: every row of every head against the oracle's selection (the
+    near-tie rule: rows whose oracle cut margin is below 1e-4 relative may
+    differ inside that band; they are counted).  O and LSE (fp32 output of
+    the forward on the GPU's own block lists): every query row of the
+    oracle's sampled heads whose mask row equals the oracle's, against the
+    oracle's attention."""
+    import numpy as np
+    from oracle import ba_att_oracle as orc
+    from oracle.parity import LSE_TOL, O_TOL, compare_masks, max_abs
+
+    t0 = time.perf_counter()
+    ref = orc.select_oracle(x["q"], x["k"], w.block, sp)
+    sel_s = time.perf_counter() - t0
+    m = compare_masks(gmask, ref["S"], ref["mask"], ref["keep"])
+    worst_o = worst_l = 0.0
+    rows = skipped = 0
+    for (bi, hi), (omask, O, L) in oracle_heads.items():
+        eq = np.all(gmask[bi, hi] == omask, axis=-1)
+        tok = np.repeat(eq, w.block)[:w.N]
+        rows += int(tok.sum())
+        skipped += int((~tok).sum())
+        worst_o = max(worst_o, max_abs(o_own[(bi, hi)][tok], O[tok]))
+        worst_l = max(worst_l, max_abs(lse_own[(bi, hi)][tok], L[tok]))
+    ok = not m["bad"] and worst_o <= O_TOL and worst_l <= LSE_TOL
+    return {"mask_rows": m["rows"], "mask_exact": m["exact"], "near_tie_rows": m["near_tie_rows"],
+            "near_tie_mismatch": m["near_tie_mismatch"], "bad_rows": len(m["bad"]),
+            "heads_o_lse": [list(h) for h in oracle_heads], "o_rows_compared": rows,
+            "o_rows_skipped_near_tie": skipped, "max_abs_dO": worst_o, "max_abs_dLSE": worst_l,
+            "tolerance": {"O": O_TOL, "LSE": LSE_TOL, "near_tie_rel_margin": 1e-4},
+            "oracle_select_all_heads_s": round(sel_s, 3), "pass": bool(ok)}
 
 
 def parse_amd_smi_metric(text: str) -> dict:
@@ -394,6 +458,171 @@ def measured_peaks(dev, stream, reps: int = 5) -> dict:
     }
 
 
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def time_steps(select, sparse, stream, warmup: int, steps: int) -> tuple:
+    """`steps` select + sparse steps back to back with no event between the
+    kernels (each event recorded between two kernels leaves about 5 us of idle
+    GPU), wall clock between two synchronisations; one event pair around the
+    whole loop cross-checks it on the GPU's clock.  Returns (ms, gpu ms) per
+    step."""
+    import torch
+    for _ in range(warmup):
+        select()
+        sparse()
+    torch.cuda.synchronize()
+    g0, g1 = _ev(), _ev()
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for _ in range(steps):
+        select()
+        sparse()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, g0.elapsed_time(g1) / steps
+
+
+def time_kernels(select, sparse, stream, steps: int) -> tuple:
+    """The same steps with HIP events around each kernel on the stream the
+    kernels run on: per-call durations (ms) of the select pass and of the
+    sparse attention kernel."""
+    import numpy as np
+    import torch
+    ev = [(_ev(), _ev(), _ev()) for _ in range(steps)]
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        select()
+        e1.record(stream)
+        sparse()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    return (np.array([a.elapsed_time(b) for a, b, _ in ev]), np.array([b.elapsed_time(c) for _, b, c in ev]))
+
+
+def time_flushed(fn, stream, warmup: int, reps: int, flush, sink):
+    """Per-call durations (ms) of fn, each call after a 1 GiB read that evicts
+    L2 and the MALL (a read leaves no dirty lines to write back)."""
+    import numpy as np
+    import torch
+    out = []
+    for i in range(warmup + reps):
+        torch.sum(flush, dim=0, out=sink)
+        a, b = _ev(), _ev()
+        a.record(stream)
+        fn()
+        b.record(stream)
+        if i >= warmup:
+            out.append((a, b))
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in out])
+
+
+def time_calls(fn, stream, warmup: int, reps: int) -> float:
+    """Mean duration (ms) of fn between one event pair per call."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(_ev(), _ev()) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+class Problem:
+    """One workload resident on the GPU with its outputs and C-ABI calls."""
+
+    def __init__(self, lib, name: str, sp: float | None, out_dtype: str, dev, stream, x=None):
+        import numpy as np
+        import torch
+        from block_sparse_attention_ba_amd import api, workloads
+
+        self.w = w = workloads.WORKLOADS[name]
+        self.sp = sp if sp is not None else (0.5 if 0.5 in w.sparsities else w.sparsities[0])
+        self.x = x if x is not None else workloads.make_inputs(name)
+
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.q, self.k, self.v = up(self.x["q"]), up(self.x["k"]), up(self.x["v"])
+        B, H, N, D, blk = w.B, w.H, w.N, w.D, w.block
+        self.dims = (B, H, N, D, blk)
+        self.n = api.num_blocks(N, blk)
+        self.keep = api.keep_count(self.n, self.sp)
+        self.odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+        self.code = 0 if self.odt == torch.bfloat16 else 1
+        self.ws = torch.empty(api.select_workspace_bytes(B, H, N, D, blk), dtype=torch.uint8, device=dev)
+        self.mask = torch.empty((B, H, self.n, self.n), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty((B, H, self.n, self.keep), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, H, self.n), dtype=torch.int32, device=dev)
+        self.o = torch.empty((B, H, N, D), dtype=self.odt, device=dev)
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        self.lib, self.stream, self.sptr = lib, stream, stream.cuda_stream
+        self.dense_flops = 4.0 * B * H * N * N * D
+        self.sel_bytes = (2.0 * B * H * N * D * 2 + B * H * self.n * self.n + 4.0 * B * H * self.n * self.keep
+                          + 4.0 * B * H * self.n)
+
+    def _check(self, st):
+        if st:
+            raise RuntimeError(self.lib.ba_att_status_string(st).decode())
+
+    def select(self):
+        B, H, N, D, blk = self.dims
+        self._check(self.lib.ba_att_select(B, H, N, D, blk, 0.0, self.sp, self.q.data_ptr(), self.k.data_ptr(),
+                                           self.mask.data_ptr(), self.idx.data_ptr(), self.cnt.data_ptr(), None,
+                                           self.ws.data_ptr(), self.ws.numel(), self.sptr))
+
+    def sparse(self, o=None, code=None):
+        B, H, N, D, blk = self.dims
+        o = self.o if o is None else o
+        self._check(self.lib.ba_att_forward(B, H, N, D, blk, 0.0, self.q.data_ptr(), self.k.data_ptr(),
+                                            self.v.data_ptr(), self.idx.data_ptr(), self.cnt.data_ptr(), self.keep,
+                                            o.data_ptr(), self.code if code is None else code,
+                                            self.lse.data_ptr(), self.sptr))
+
+    def dense(self):
+        B, H, N, D, blk = self.dims
+        self._check(self.lib.ba_att_dense(B, H, N, D, 0.0, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                          self.o.data_ptr(), self.code, self.lse.data_ptr(), self.sptr))
+
+    def label(self) -> str:
+        B, H, N, D, blk = self.dims
+        return f"B{B} H{H} N{N} D{D} b{blk}"
+
+
+def secondary(lib, name: str, args, dev, stream, flush, sink) -> dict:
+    """The step against the dense kernel on another workload: step time,
+    per-kernel times, the sparse kernel's and the flushed select pass's
+    roofline fractions."""
+    import numpy as np
+    import torch
+    p = Problem(lib, name, None, args.out_dtype, dev, stream)
+    step_ms, _ = time_steps(p.select, p.sparse, stream, args.warmup, args.steps)
+    sel_t, spa_t = time_kernels(p.select, p.sparse, stream, args.steps)
+    sel_f = time_flushed(p.select, stream, 5, max(10, args.steps // 2), flush, sink)
+    dense_ms = time_calls(p.dense, stream, max(5, args.warmup // 2), max(5, args.steps // 2))
+    kept = kept_tile_flops(p.mask.cpu().numpy(), p.w.N, p.w.D, p.w.block)
+    spa_ms, selm = float(spa_t.mean()), float(np.median(sel_f))
+    res = {"workload": p.w.description, "name": name, "shape": p.label(), "sparsity": p.sp,
+           "keep": p.keep, "n_blocks": p.n, "ms_per_step": round(step_ms, 5),
+           "dense_equiv_tflops": round(p.dense_flops / step_ms / 1e9, 2),
+           "dense_ms": round(dense_ms, 5), "speedup_vs_dense": round(dense_ms / step_ms, 4),
+           "select_ms": round(float(sel_t.mean()), 5), "sparse_attention_ms": round(spa_ms, 5),
+           "sparse_frac_of_mfma_peak": round(kept / (spa_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+           "select_flushed_ms": round(selm, 5),
+           "select_frac_of_hbm_peak": round(p.sel_bytes / (selm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del p
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -405,59 +634,22 @@ def main():
     import numpy as np
     import torch
 
-    from block_sparse_attention_ba_amd import _lib, api, workloads
+    from block_sparse_attention_ba_amd import _lib, api
 
     if not os.path.exists(_lib.LIB_PATH):
         from block_sparse_attention_ba_amd import build
         build.build()
     api.load()
+    lib = _lib.load()
 
-    w = workloads.WORKLOADS[args.workload]
-    sp = args.sparsity if args.sparsity is not None else (0.5 if 0.5 in w.sparsities else w.sparsities[0])
-    x = workloads.make_inputs(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    def up(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
-    B, H, N, D, blk = w.B, w.H, w.N, w.D, w.block
-    n = api.num_blocks(N, blk)
-    keep = api.keep_count(n, sp)
-    odt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
-    ws = torch.empty(api.select_workspace_bytes(B, H, N, D, blk), dtype=torch.uint8, device=dev)
-    mask = torch.empty((B, H, n, n), dtype=torch.uint8, device=dev)
-    idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, H, n), dtype=torch.int32, device=dev)
-    o = torch.empty((B, H, N, D), dtype=odt, device=dev)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    lib = _lib.load()
     stream = torch.cuda.current_stream(dev)
-    sptr = stream.cuda_stream
-    code = 0 if odt == torch.bfloat16 else 1
-
-    def select():
-        st = lib.ba_att_select(B, H, N, D, blk, 0.0, sp, q.data_ptr(), k.data_ptr(), mask.data_ptr(),
-                               idx.data_ptr(), cnt.data_ptr(), None, ws.data_ptr(), ws.numel(), sptr)
-        if st:
-            raise RuntimeError(lib.ba_att_status_string(st).decode())
-
-    def sparse():
-        st = lib.ba_att_forward(B, H, N, D, blk, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                idx.data_ptr(), cnt.data_ptr(), keep, o.data_ptr(), code,
-                                lse.data_ptr(), sptr)
-        if st:
-            raise RuntimeError(lib.ba_att_status_string(st).decode())
-
-    def dense():
-        st = lib.ba_att_dense(B, H, N, D, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              o.data_ptr(), code, lse.data_ptr(), sptr)
-        if st:
-            raise RuntimeError(lib.ba_att_status_string(st).decode())
-
-    print(f"[bench] workload {w.name}: B{B} H{H} N{N} D{D} block {blk} sparsity {sp} keep {keep}/{n}",
-          file=sys.stderr, flush=True)
+    P = Problem(lib, args.workload, args.sparsity, args.out_dtype, dev, stream)
+    w, sp = P.w, P.sp
+    B, H, N, D, blk = P.dims
+    n, keep = P.n, P.keep
+    print(f"[bench] workload {w.name}: {P.label()} sparsity {sp} keep {keep}/{n}", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         # a plain copy of known size in one elementwise dispatch (a uint8 ->
@@ -469,165 +661,113 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- the timed hot path: K steps of select + sparse attention, back to
-    # back with no event between the kernels (each event record between two
-    # kernels leaves about 5 us of idle GPU), wall clock between two
-    # synchronisations; one event pair around the whole loop cross-checks it
-    for _ in range(args.warmup):
-        select()
-        sparse()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g0.record(stream)
-    for _ in range(args.steps):
-        select()
-        sparse()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = wall * 1e3 / args.steps
-    gpu_step_ms = g0.elapsed_time(g1) / args.steps
-
-    # ---- the same K steps again with HIP events around each kernel on its
-    # stream: the per-kernel durations (and the sparse kernel's roofline)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        select()
-        e1.record(stream)
-        sparse()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    sel_t = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    spa_t = np.array([b.elapsed_time(c) for _, b, c in ev])
+    # ---- the timed hot path
+    step_ms, gpu_step_ms = time_steps(P.select, P.sparse, stream, args.warmup, args.steps)
+    sel_t, spa_t = time_kernels(P.select, P.sparse, stream, args.steps)
     sel_ms, spa_ms = float(sel_t.mean()), float(spa_t.mean())
     pct = lambda t: [round(float(np.percentile(t, 10)), 5), round(float(np.percentile(t, 90)), 5)]
     print(f"[bench] timed {args.steps} steps: {step_ms:.4f} ms/step ({gpu_step_ms:.4f} ms between GPU events); "
           f"per kernel over {args.steps} more steps: select {sel_ms:.4f} ms, sparse attention {spa_ms:.4f} ms",
           file=sys.stderr, flush=True)
 
-    mask_np = mask.cpu().numpy()
-    kept_flops = kept_tile_flops(mask_np, N, D, blk)
-    dense_flops = 4.0 * B * H * N * N * D
+    gmask = P.mask.cpu().numpy()
+    kept_flops = kept_tile_flops(gmask, N, D, blk)
 
-    # ---- selection pass with L2 and the MALL flushed by reading 1 GiB of
-    # unrelated data (a read leaves no dirty lines to write back)
+    # ---- selection pass with L2 and the MALL flushed before every call
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
-    sel_flushed = []
-    for i in range(args.warmup + args.steps):
-        torch.sum(flush, dim=0, out=sink)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        select()
-        b.record(stream)
-        if i >= args.warmup:
-            sel_flushed.append((a, b))
-    torch.cuda.synchronize()
-    sel_flush_t = np.array([a.elapsed_time(b) for a, b in sel_flushed])
+    sel_flush_t = time_flushed(P.select, stream, args.warmup, args.steps, flush, sink)
     sel_flush_ms = float(np.median(sel_flush_t))
-    sel_bytes = 2.0 * B * H * N * D * 2 + B * H * n * n + 4.0 * B * H * n * keep + 4.0 * B * H * n
 
     # ---- the dense comparator
     dense_ms = None
     if not args.skip_dense:
-        for _ in range(args.warmup):
-            dense()
-        torch.cuda.synchronize()
-        evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(max(5, args.steps // 2))]
-        for a, b in evd:
-            a.record(stream)
-            dense()
-            b.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in evd]))
-        print(f"[bench] dense {dense_ms:.4f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s)",
+        dense_ms = time_calls(P.dense, stream, args.warmup, max(5, args.steps // 2))
+        print(f"[bench] dense {dense_ms:.4f} ms ({P.dense_flops / dense_ms / 1e9:.1f} TFLOP/s)",
               file=sys.stderr, flush=True)
 
     # ---- the step and the dense comparator again, each repetition after the
-    # same 1 GiB flushing read (no input left in L2 or the MALL)
+    # same flushing read (no input left in L2 or the MALL)
     flushed = None
     if not args.skip_flushed and not args.skip_dense:
         reps = max(10, args.steps // 2)
-        ev_step, ev_dense = [], []
-        for _ in range(reps):
-            torch.sum(flush, dim=0, out=sink)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record(stream)
-            select()
-            sparse()
-            e[1].record(stream)
-            ev_step.append(e)
-        for _ in range(reps):
-            torch.sum(flush, dim=0, out=sink)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record(stream)
-            dense()
-            e[1].record(stream)
-            ev_dense.append(e)
-        torch.cuda.synchronize()
-        f_step = np.array([e[0].elapsed_time(e[1]) for e in ev_step])
-        f_dense = np.array([e[0].elapsed_time(e[1]) for e in ev_dense])
+        f_step = time_flushed(lambda: (P.select(), P.sparse()), stream, 0, reps, flush, sink)
+        f_dense = time_flushed(P.dense, stream, 0, reps, flush, sink)
         fs, fd = float(np.median(f_step)), float(np.median(f_dense))
         flushed = {"reps": reps, "flush": "1 GiB read before each repetition",
                    "step_ms": round(fs, 5), "dense_ms": round(fd, 5),
                    "speedup_vs_dense": round(fd / fs, 4),
-                   "dense_equiv_tflops": round(dense_flops / (fs * 1e-3) / 1e12, 2),
+                   "dense_equiv_tflops": round(P.dense_flops / (fs * 1e-3) / 1e12, 2),
                    "p10_p90_ms": {"step": pct(f_step), "dense": pct(f_dense)}}
         print(f"[bench] flushed: {flushed}", file=sys.stderr, flush=True)
-    del flush, sink
 
     power = None
     if args.power:
-        power = {"sparse": power_sample(sparse, stream, 4.0), "dense": power_sample(dense, stream, 4.0)}
+        power = {"sparse": power_sample(P.sparse, stream, 4.0), "dense": power_sample(P.dense, stream, 4.0)}
         print(f"[bench] power: {power}", file=sys.stderr, flush=True)
+
+    # ---- the product path's own outputs for the parity check against the
+    # oracle: the forward on the GPU's block lists with fp32 output
+    heads = sample_heads(w.name, B, H, args.cpu_heads)
+    own_o = own_l = None
+    if not args.skip_cpu:
+        P.select()
+        o32 = torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+        P.sparse(o=o32, code=1)
+        torch.cuda.synchronize()
+        gmask = P.mask.cpu().numpy()
+        own_o = {h: o32[h[0], h[1]].cpu().numpy() for h in heads}
+        own_l = {h: P.lse[h[0], h[1]].cpu().numpy() for h in heads}
+        del o32
 
     split_kv = external = None
     if not args.skip_split:
         split_kv = split_kv_measurement(lib, dev, stream, args.warmup, max(5, args.steps // 2))
         print(f"[bench] split key lists: {split_kv}", file=sys.stderr, flush=True)
-        external = external_measurement(lib, stream, (B, H, N, D, blk, keep, code),
-                                        (q, k, v, idx, cnt, o, lse), 10, max(5, args.steps // 2))
+        external = external_measurement(lib, stream, (B, H, N, D, blk, keep, P.code),
+                                        (P.q, P.k, P.v, P.idx, P.cnt, P.o, P.lse), 10, max(5, args.steps // 2))
         print(f"[bench] external contribution: {external}", file=sys.stderr, flush=True)
+
+    quality = None
+    if not args.skip_quality:
+        from block_sparse_attention_ba_amd import quality as qmod
+        quality = qmod.measure(P.q, P.k, P.v, blk, sp)
+        print(f"[bench] selection quality: {quality}", file=sys.stderr, flush=True)
+
+    extra = []
+    for name in [e for e in args.extra.split(",") if e and e != w.name]:
+        extra.append(secondary(lib, name, args, dev, stream, flush, sink))
+        print(f"[bench] {name}: {extra[-1]}", file=sys.stderr, flush=True)
 
     sweep = None
     if not args.skip_sweep:
         sweep = long_context_sweep(dev, stream, 5, 10)
         print(f"[bench] long-context sweep: {sweep}", file=sys.stderr, flush=True)
+    del flush, sink
 
     peaks = None
     if not args.skip_peaks:
         peaks = measured_peaks(dev, stream)
         print(f"[bench] measured peaks: {peaks}", file=sys.stderr, flush=True)
 
-    quality = None
-    if not args.skip_quality:
-        from block_sparse_attention_ba_amd import quality as qmod
-        quality = qmod.measure(q, k, v, blk, sp)
-        print(f"[bench] selection quality: {quality}", file=sys.stderr, flush=True)
-
-    # ---- HBM traffic from the committed counter runs, if they match these kernels
-    traffic = None
-    src_hash = kernel_source_hash()
+    # ---- HBM traffic from the committed counter runs, while the kernels'
+    # sources still match the ones the counters were taken on
+    traffic = sel_traffic = None
+    hashes = {kind: kernel_source_hash(kind) for kind in KERNEL_SOURCES}
     try:
         with open(TRAFFIC_FILE) as f:
             tc = json.load(f)
-        entry = tc.get("workloads", {}).get(f"{w.name}:{sp}:{args.out_dtype}")
-        if tc.get("kernel_source_hash") == src_hash and entry:
+        entry = tc.get("workloads", {}).get(f"{w.name}:{sp}:{args.out_dtype}") or {}
+        if entry.get("attention_source_hash") == hashes["attention"]:
             traffic = entry.get("attention_bytes_per_launch")
+        if entry.get("select_source_hash") == hashes["select"]:
             sel_traffic = entry.get("select_bytes_per_call")
-        else:
-            sel_traffic = None
     except (OSError, ValueError):
-        sel_traffic = None
+        pass
 
     achieved = kept_flops / (spa_ms * 1e-3) / 1e12
-    value = dense_flops / (step_ms * 1e-3) / 1e12
-    sel_gbs = sel_bytes / (sel_flush_ms * 1e-3) / 1e9
+    value = P.dense_flops / (step_ms * 1e-3) / 1e12
+    sel_gbs = P.sel_bytes / (sel_flush_ms * 1e-3) / 1e9
     result = {
         "metric": "dense-equiv attention TFLOP/s + speedup vs own dense kernel @50% sparsity",
         "value": round(value, 3),
@@ -647,7 +787,7 @@ def main():
                    "out_dtype": args.out_dtype, "parallelism": "single GPU"},
         "speedup_vs_dense": round(dense_ms / step_ms, 4) if dense_ms else None,
         "dense_ms": round(dense_ms, 5) if dense_ms else None,
-        "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
+        "dense_tflops": round(P.dense_flops / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "select_ms": round(sel_ms, 5),
         "sparse_attention_ms": round(spa_ms, 5),
         "p10_p90_ms": {"select": pct(sel_t), "sparse_attention": pct(spa_t), "select_flushed": pct(sel_flush_t)},
@@ -658,24 +798,27 @@ def main():
         "roofline_select": {"bound": "hbm", "kernel": "pool_stats_kernel + score_topk_kernel",
                             "achieved": round(sel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,
-                            "bytes_per_call": sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
+                            "bytes_per_call": P.sel_bytes, "ms_flushed_median": round(sel_flush_ms, 5)},
         "flushed": flushed,
+        "other_workloads": extra,
+        "long_context_sweep": sweep,
         "measured_peaks": peaks,
         "split_kv": split_kv,
         "external": external,
         "power": power,
-        "long_context_sweep": sweep,
         "selection_quality": quality,
         # the pages' only operator-speed figure, as context: it names no hardware,
         # sequence length or sparsity, so it is no target for this measurement
         "paper_context": "up to 6.95x over FlashAttention (hardware, shape and sparsity not stated)",
-        "kernel_source_hash": src_hash,
+        "kernel_source_hash": hashes,
     }
+    result["cpu_baseline"] = result["parity"] = None
     if not args.skip_cpu:
-        print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(x, w, sp, args.cpu_seconds)
-    else:
-        result["cpu_baseline"] = None
+        print(f"[bench] timing the CPU oracle on {len(heads)} heads ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"], oracle_heads = cpu_baseline(P.x, w, sp, heads)
+        print(f"[bench] cpu baseline: {result['cpu_baseline']}", file=sys.stderr, flush=True)
+        result["parity"] = parity_report(P.x, w, sp, gmask, own_o, own_l, oracle_heads)
+        print(f"[bench] parity: {result['parity']}", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
 
 
