@@ -17,8 +17,9 @@
 namespace {
 
 constexpr int kMaxN = 1 << 20;
-constexpr int kMaxBlocksPerRow = 1024;  // mask -> index rows
+constexpr int kMaxBlocksPerRow = 2048;  // mask -> index rows
 constexpr int kMaxSelectBlocks = ba::kMaxScoreBlocks;
+constexpr int kMaxFullScoreBlocks = 512;  // the full-covariance diagnostic
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -38,11 +39,17 @@ float resolve_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sq
 
 int round_up8(int x) { return (x + 7) / 8 * 8; }
 
+// keep = n - floor(sparsity*n + 1e-9), clamped to [1, n] (valid n, sparsity)
+int keep_count(int n, double sparsity) {
+  const long long drop = (long long)floor(sparsity * (double)n + 1e-9);
+  return (int)std::min<long long>(n, std::max<long long>(1, (long long)n - drop));
+}
+
 ba_status finish_launch() {
   return hipGetLastError() == hipSuccess ? BA_OK : BA_ERR_HIP;
 }
 
-int ni_for(int n) {  // elements per lane for a row of n blocks: 1, 2, 4, 8 or 16
+int ni_for(int n) {  // elements per lane for a row of n blocks: 1, 2, 4, ..., 32
   int ni = 1;
   while (ni * 64 < n) ni *= 2;
   return ni;
@@ -58,14 +65,46 @@ void launch_pool(int BH, int N, int n, int block, float scale, const uint16_t* q
     ba::pool_stats_kernel<D, 128><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
 }
 
+// Rows per score workgroup: the largest R in {64, 32, 16} whose grid of
+// B*H*ceil(n/R) workgroups still covers every compute unit and whose row
+// buffers fit the LDS (each workgroup reads its head's ak once, so fewer,
+// taller workgroups re-read it less); 16 when none covers the device.
+int score_rows(int BH, int n, int D, int NI) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  for (int R : {64, 32}) {
+    const int ctw = NI >= 4 ? NI / 4 : 1;
+    if ((R / 16) * ctw > 8 || ba::score_lds_bytes(D, R, n) > ba::kScoreLdsBytes) continue;
+    if ((long long)BH * ((n + R - 1) / R) >= cus) return R;
+  }
+  return 16;
+}
+
+template <int D, int NI, int R>
+void launch_score_r(int BH, int n, int keep, const float* aq, const float* ak, uint8_t* mask,
+                    int32_t* idx, int32_t* cnt, float* score, hipStream_t s) {
+  const int total = BH * ((n + R - 1) / R);
+  const size_t smem = (size_t)ba::score_lds_bytes(D, R, n);
+  if (smem > 65536)  // beyond the default dynamic-LDS limit of a launch
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&ba::score_topk_kernel<D, NI, R>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  ba::score_topk_kernel<D, NI, R><<<dim3(round_up8(total)), ba::kScoreWaves * 64, smem, s>>>(
+      aq, ak, n, keep, mask, idx, cnt, score, total);
+}
+
 template <int D, int NI>
 void launch_score_ni(int BH, int n, int keep, const float* aq, const float* ak, uint8_t* mask,
                      int32_t* idx, int32_t* cnt, float* score, hipStream_t s) {
-  const int tiles = (n + ba::kScoreRows - 1) / ba::kScoreRows;
-  const int total = BH * tiles;
-  const size_t smem = (size_t)ba::kScoreRows * n * sizeof(float);
-  ba::score_topk_kernel<D, NI><<<dim3(round_up8(total)), ba::kScoreWaves * 64, smem, s>>>(
-      aq, ak, n, keep, mask, idx, cnt, score, total);
+  const int R = score_rows(BH, n, D, NI);
+  if constexpr (NI <= 4) {
+    if (R == 64) return launch_score_r<D, NI, 64>(BH, n, keep, aq, ak, mask, idx, cnt, score, s);
+  }
+  if constexpr (NI <= 16) {
+    if (R == 32) return launch_score_r<D, NI, 32>(BH, n, keep, aq, ak, mask, idx, cnt, score, s);
+  }
+  launch_score_r<D, NI, 16>(BH, n, keep, aq, ak, mask, idx, cnt, score, s);
 }
 
 template <int D>
@@ -76,7 +115,8 @@ void launch_score(int BH, int n, int keep, const float* aq, const float* ak, uin
     case 2: launch_score_ni<D, 2>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
     case 4: launch_score_ni<D, 4>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
     case 8: launch_score_ni<D, 8>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
-    default: launch_score_ni<D, 16>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
+    case 16: launch_score_ni<D, 16>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
+    default: launch_score_ni<D, 32>(BH, n, keep, aq, ak, mask, idx, cnt, score, s); break;
   }
 }
 
@@ -87,6 +127,45 @@ void launch_attn(const ba::AttnParams& p, bool out_f32, hipStream_t s) {
     ba::attn_fwd_kernel<D, WAVES, BLK, SPARSE, true><<<grid, WAVES * 64, 0, s>>>(p);
   else
     ba::attn_fwd_kernel<D, WAVES, BLK, SPARSE, false><<<grid, WAVES * 64, 0, s>>>(p);
+}
+
+// Checks of ba_att_select's arguments other than its workspace.
+ba_status check_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, double sparsity,
+                       const void* q, const void* k, const uint8_t* block_mask, const int32_t* block_idx,
+                       const int32_t* block_cnt, const float* score) {
+  ba_status st = check_shape(B, H, N, D);
+  if (st != BA_OK) return st;
+  if (!q || !k || !block_mask || !block_idx || !block_cnt) return BA_ERR_INVALID_ARG;
+  if (!(sparsity >= 0.0 && sparsity < 1.0)) return BA_ERR_INVALID_ARG;
+  if (block != 64 && block != 128) return BA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(block_idx, 4) || !aligned(block_cnt, 4) ||
+      (score && !aligned(score, 4)))
+    return BA_ERR_INVALID_ARG;
+  if (num_blocks(N, block) > kMaxSelectBlocks) return BA_ERR_UNSUPPORTED;
+  return BA_OK;
+}
+
+// The selection pass with the pooled statistics at ws: aq [B*H, n, 3D] then
+// ak [B*H, n, 3D], fp32 (checked arguments).
+ba_status launch_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                        double sparsity, const void* q, const void* k, uint8_t* block_mask,
+                        int32_t* block_idx, int32_t* block_cnt, float* score, float* ws, hipStream_t s) {
+  const int n = num_blocks(N, block);
+  const int keep = keep_count(n, sparsity);
+  const int BH = B * H;
+  const float sc = resolve_scale(scale, D);
+  float* aq = ws;
+  float* ak = aq + (size_t)BH * n * 3 * D;
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  if (D == 128) {
+    launch_pool<128>(BH, N, n, block, sc, q16, k16, aq, ak, s);
+    launch_score<128>(BH, n, keep, aq, ak, block_mask, block_idx, block_cnt, score, s);
+  } else {
+    launch_pool<64>(BH, N, n, block, sc, q16, k16, aq, ak, s);
+    launch_score<64>(BH, n, keep, aq, ak, block_mask, block_idx, block_cnt, score, s);
+  }
+  return finish_launch();
 }
 
 }  // namespace
@@ -100,11 +179,7 @@ int32_t ba_att_num_blocks(int32_t N, int32_t block) {
 
 int32_t ba_att_keep_count(int32_t n_blocks, double sparsity) {
   if (n_blocks < 1 || !(sparsity >= 0.0 && sparsity < 1.0)) return -1;
-  const long long drop = (long long)floor(sparsity * (double)n_blocks + 1e-9);
-  long long keep = (long long)n_blocks - drop;
-  if (keep < 1) keep = 1;
-  if (keep > n_blocks) keep = n_blocks;
-  return (int32_t)keep;
+  return keep_count(n_blocks, sparsity);
 }
 
 size_t ba_att_select_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block) {
@@ -117,34 +192,12 @@ int ba_att_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, flo
                   double sparsity, const void* q, const void* k, uint8_t* block_mask,
                   int32_t* block_idx, int32_t* block_cnt, float* score, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  ba_status st = check_shape(B, H, N, D);
+  ba_status st = check_select(B, H, N, D, block, sparsity, q, k, block_mask, block_idx, block_cnt, score);
   if (st != BA_OK) return st;
-  if (!q || !k || !block_mask || !block_idx || !block_cnt) return BA_ERR_INVALID_ARG;
-  if (!(sparsity >= 0.0 && sparsity < 1.0)) return BA_ERR_INVALID_ARG;
-  if (block != 64 && block != 128) return BA_ERR_UNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(block_idx, 4) || !aligned(block_cnt, 4) ||
-      (score && !aligned(score, 4)))
-    return BA_ERR_INVALID_ARG;
-  const int n = num_blocks(N, block);
-  if (n > kMaxSelectBlocks) return BA_ERR_UNSUPPORTED;
   const size_t need = ba_att_select_workspace_bytes(B, H, N, D, block);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return BA_ERR_WORKSPACE;
-  const int keep = ba_att_keep_count(n, sparsity);
-  const int BH = B * H;
-  const float sc = resolve_scale(scale, D);
-  float* aq = static_cast<float*>(workspace);
-  float* ak = aq + (size_t)BH * n * 3 * D;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint16_t* q16 = static_cast<const uint16_t*>(q);
-  const uint16_t* k16 = static_cast<const uint16_t*>(k);
-  if (D == 128) {
-    launch_pool<128>(BH, N, n, block, sc, q16, k16, aq, ak, s);
-    launch_score<128>(BH, n, keep, aq, ak, block_mask, block_idx, block_cnt, score, s);
-  } else {
-    launch_pool<64>(BH, N, n, block, sc, q16, k16, aq, ak, s);
-    launch_score<64>(BH, n, keep, aq, ak, block_mask, block_idx, block_cnt, score, s);
-  }
-  return finish_launch();
+  return launch_select(B, H, N, D, block, scale, sparsity, q, k, block_mask, block_idx, block_cnt, score,
+                       static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* block_mask,
@@ -162,7 +215,8 @@ int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* 
     case 2: ba::mask_to_index_kernel<2><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
     case 4: ba::mask_to_index_kernel<4><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
     case 8: ba::mask_to_index_kernel<8><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
-    default: ba::mask_to_index_kernel<16><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
+    case 16: ba::mask_to_index_kernel<16><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
+    default: ba::mask_to_index_kernel<32><<<grid, 256, 0, s>>>(block_mask, (int)rows, n_blocks, max_keep, block_idx, block_cnt); break;
   }
   return finish_launch();
 }
@@ -447,7 +501,7 @@ int ba_att_block_map(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, 
 size_t ba_att_score_full_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block) {
   if (check_shape(B, H, N, D) != BA_OK || (block != 64 && block != 128)) return 0;
   const int n = num_blocks(N, block);
-  if (n > kMaxSelectBlocks) return 0;
+  if (n > kMaxFullScoreBlocks) return 0;
   const int BH = B * H;
   const FullPlan f = full_plan(BH, n, D);
   return (2 * (size_t)BH * n * f.kf + (size_t)f.parts * BH * n * n) * sizeof(float);
@@ -463,7 +517,7 @@ int ba_att_score_full(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(s_full, 4) || (s_mean && !aligned(s_mean, 4)))
     return BA_ERR_INVALID_ARG;
   const int n = num_blocks(N, block);
-  if (n > kMaxSelectBlocks) return BA_ERR_UNSUPPORTED;
+  if (n > kMaxFullScoreBlocks) return BA_ERR_UNSUPPORTED;
   const size_t need = ba_att_score_full_workspace_bytes(B, H, N, D, block);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return BA_ERR_WORKSPACE;
   const int BH = B * H;

@@ -147,19 +147,29 @@ __global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Compact score and norm sort.  One workgroup per (b*h, 16 query-block
-// rows, 16 waves).  S = aq . ak^T is a small fp32 GEMM (K = 3D) done with
-// v_mfma_f32_16x16x4_f32: wave w sums half (w % 2) of the dot products for
-// the 16x16 output tiles w/2, w/2 + 8, ...; operands are loaded from L2 as
-// float4 (lane group g = l/16 takes k = 16m + 4g + e for MFMA step (m, e),
-// the same assignment for both operands, so the product is unchanged).  The
-// first halves are written to LDS and the second halves added after a
-// barrier; then one wave per row selects the `keep` largest scores (ties to
-// lower J) by an MSB-first radix select over order-preserving uint32 keys and
-// writes mask, ascending idx and cnt.
+// Compact score and norm sort.  One workgroup of 16 waves per (b*h, R
+// consecutive query-block rows), R in {16, 32, 64} chosen by the host so that
+// the grid still covers the device: every workgroup reads its head's ak once,
+// so larger R means fewer re-reads of ak.
+//
+// S = aq . ak^T is a small fp32 GEMM (K = 3D) done with
+// v_mfma_f32_16x16x4_f32 on 16x16 output tiles.  Wave w owns the column
+// tiles w, w + 16, ... and every row tile of them, so the B operand (ak,
+// loaded from L2 as float4 per lane) is read once per workgroup and reused
+// for the R/16 row tiles; the A operand (aq) is staged in LDS in two halves
+// of K, its float4 slots XOR-swizzled by the row so that the 16 rows of a
+// tile hit distinct banks.  Lane group g takes k = 16m + 4g + e for MFMA
+// step (m, e) in both operands (a permutation of k, so the product is
+// unchanged); every tile accumulates its K steps in the same order whatever
+// R is, so S does not depend on R.  The accumulators stay in registers over
+// both halves and then go to an LDS row buffer [R][n + 4]; one wave per row
+// then selects the `keep` largest scores (ties to lower J) by an MSB-first
+// radix select over order-preserving uint32 keys and writes mask, ascending
+// idx and cnt.
 // ---------------------------------------------------------------------------
-constexpr int kScoreRows = 16;
-constexpr int kMaxScoreBlocks = 512;  // longest row: 16 rows x n fp32 scores staged in LDS
+constexpr int kMaxScoreBlocks = 2048;  // longest row
+constexpr int kScoreWaves = 16;
+constexpr int kScoreLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = __lane_id();
@@ -274,11 +284,13 @@ __device__ __forceinline__ void radix_select_row(const uint32_t (&key)[NI], int 
   if (lane == 0) *cnt_out = base;
 }
 
-constexpr int kScoreWaves = 16;
-constexpr int kScoreColWaves = 8;  // waves per half of the dot products
-constexpr int kMaxColRounds = (kMaxScoreBlocks + 16 * kScoreColWaves - 1) / (16 * kScoreColWaves);
+// LDS bytes of one score workgroup: the A half-tile [R][3D/2] and the score
+// rows [R][n + 4] (fp32).
+__host__ __device__ constexpr int score_lds_bytes(int D, int R, int n) {
+  return (R * (3 * D / 2) + R * (n + 4)) * 4;
+}
 
-template <int D, int NI>
+template <int D, int NI, int R>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const float* __restrict__ aq,
                                                          const float* __restrict__ ak, int n,
                                                          int keep, uint8_t* __restrict__ mask,
@@ -286,12 +298,18 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
                                                          int32_t* __restrict__ cnt,
                                                          float* __restrict__ score, int total) {
   constexpr int K3 = 3 * D;
-  constexpr int KH = K3 / 2;         // each wave takes one half of the 3D-long dot products
-  constexpr int KM = KH / 16;        // float4 operand loads per 16x16 tile and half
-  constexpr int R = kScoreRows;
-  constexpr int AP = K3 + 4;         // padded LDS row pitch of the A tile (floats)
-  __shared__ __attribute__((aligned(16))) float Atile[R * AP];
-  extern __shared__ float Sbuf[];    // [R][n]
+  constexpr int KCH = K3 / 2;         // floats of an A row staged at a time
+  constexpr int F4 = KCH / 4;         // float4 slots per staged A row
+  constexpr int SWZ = (F4 % 16 == 0) ? 15 : 7;  // slot swizzle within aligned groups of F4
+  static_assert(F4 % (SWZ + 1) == 0, "swizzle must stay inside the row");
+  constexpr int MST = KCH / 16;       // float4 B loads per lane per half and column tile
+  constexpr int RT = R / 16;          // row tiles
+  constexpr int CTW = NI >= 4 ? NI / 4 : 1;  // column tiles per wave (4*NI tiles cover 64*NI columns)
+  static_assert(RT * CTW <= 8, "accumulators of a wave");
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  float* const Abuf = lds;                  // [R][KCH], float4 slot j of row r at j ^ (r & SWZ)
+  float* const Sbuf = lds + R * KCH;        // [R][SP]
+  const int SP = n + 4;
 
   // the row tiles of one head run on one XCD and share its L2 copy of ak
   const int logical = xcd_remap(blockIdx.x, total);
@@ -302,71 +320,68 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  const int half = wave & 1;               // which half of k this wave sums
-  const int cw = wave >> 1;                // column-tile lane of the wave: tiles cw, cw + 8, ...
-
-  // stage the 16 query-block rows of aq once (coalesced float4)
-  for (int e = threadIdx.x; e < R * (K3 / 4); e += kScoreWaves * 64) {
-    const int row = e / (K3 / 4), k4 = e % (K3 / 4);
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (R0 + row < n) v = *reinterpret_cast<const f32x4*>(aq + ((size_t)bh * n + R0 + row) * K3 + 4 * k4);
-    *reinterpret_cast<f32x4*>(Atile + row * AP + 4 * k4) = v;
-  }
-
   const int ctiles = (n + 15) / 16;
-  auto load_b = [&](int ct, f32x4 (&bfr)[KM]) {
-    const int col = ct * 16 + li;
-    const float* Bp = ak + ((size_t)bh * n + col) * K3 + half * KH + 4 * lg;
+  const float* const Ah = aq + ((size_t)bh * n + R0) * K3;
+  const float* const Bh = ak + (size_t)bh * n * K3;
+
+  f32x4 acc[CTW][RT];
 #pragma unroll
-    for (int m = 0; m < KM; ++m)
-      bfr[m] = col < n ? *reinterpret_cast<const f32x4*>(Bp + 16 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  f32x4 bfr[KM];
-  if (cw < ctiles) load_b(cw, bfr);  // in flight while the A tile is staged
-  __syncthreads();
-  // first half: straight into Sbuf; second half: kept in registers, added
-  // after a barrier (a fixed order, so the sum is deterministic)
-  f32x4 acc2[kMaxColRounds];
+  for (int t = 0; t < CTW; ++t)
 #pragma unroll
-  for (int t = 0; t < kMaxColRounds; ++t) {
-    const int ct = cw + kScoreColWaves * t;
-    acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ct >= ctiles) continue;
-    if (t > 0) load_b(ct, bfr);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RT; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(Atile + li * AP + half * KH + 16 * m + 4 * lg);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bfr[m][e], acc, 0, 0, 0);
+  for (int h = 0; h < 2; ++h) {
+    if (h > 0) __syncthreads();  // every wave is done with the first half
+    for (int e = threadIdx.x; e < R * F4; e += kScoreWaves * 64) {
+      const int row = e / F4, j = e - row * F4;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (R0 + row < n) v = *reinterpret_cast<const f32x4*>(Ah + (size_t)row * K3 + h * KCH + 4 * j);
+      *reinterpret_cast<f32x4*>(Abuf + row * KCH + 4 * (j ^ (row & SWZ))) = v;
     }
-    // lane holds column ct*16 + li of rows 4*lg + r
-    const int col = ct * 16 + li;
-    if (half == 0) {
-      if (col < n) {
+    __syncthreads();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Sbuf[(4 * lg + r) * n + col] = acc[r];
+    for (int t = 0; t < CTW; ++t) {
+      const int ct = wave + kScoreWaves * t;
+      if (ct >= ctiles) break;
+      // one column tile's B operand in flight at a time (loads hoisted from
+      // later tiles would spill the accumulators of long rows)
+      __builtin_amdgcn_sched_barrier(0);
+      const int col = ct * 16 + li;
+      const float* Bp = Bh + (size_t)col * K3 + h * KCH + 4 * lg;
+      f32x4 b[MST];
+#pragma unroll
+      for (int m = 0; m < MST; ++m)
+        b[m] = col < n ? *reinterpret_cast<const f32x4*>(Bp + 16 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < MST; ++m) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const int row = r * 16 + li;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(Abuf + row * KCH + 4 * ((4 * m + lg) ^ (row & SWZ)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[m][e], acc[t][r], 0, 0, 0);
+        }
       }
-    } else {
-      acc2[t] = acc;
     }
   }
-  __syncthreads();
-  if (half == 1) {
+  // lane holds column ct*16 + li of rows r*16 + 4*lg + {0..3}
 #pragma unroll
-    for (int t = 0; t < kMaxColRounds; ++t) {
-      const int col = (cw + kScoreColWaves * t) * 16 + li;
-      if (col < n) {
+  for (int t = 0; t < CTW; ++t) {
+    const int ct = wave + kScoreWaves * t;
+    const int col = ct * 16 + li;
+    if (ct < ctiles && col < n) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Sbuf[(4 * lg + r) * n + col] += acc2[t][r];
-      }
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Sbuf[(r * 16 + 4 * lg + q) * SP + col] = acc[t][r][q];
     }
   }
   __syncthreads();
   if (score != nullptr) {  // the score map as the selection saw it, row by row
     for (int e = threadIdx.x; e < R * n; e += kScoreWaves * 64) {
       const int row = e / n, col = e - row * n;
-      if (R0 + row < n) score[((size_t)bh * n + R0 + row) * n + col] = Sbuf[e];
+      if (R0 + row < n) score[((size_t)bh * n + R0 + row) * n + col] = Sbuf[row * SP + col];
     }
   }
 
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int J = lane + 64 * i;
-      key[i] = (J < n) ? float_order_key(Sbuf[r * n + J]) : 0u;
+      key[i] = (J < n) ? float_order_key(Sbuf[r * SP + J]) : 0u;
     }
     const size_t row = (size_t)bh * n + I;
     radix_select_row<NI>(key, n, keep, mask + row * n, idx + row * keep, cnt + row);

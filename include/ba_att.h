@@ -31,7 +31,11 @@
  *    [B, H, n].
  *  - scale <= 0 selects the default softmax scale 1/sqrt(D).
  *  - Supported: D in {64, 128}; block in {64, 128}; 1 <= N <= 2^20;
- *    B*H*N*D < 2^31 elements.
+ *    B*H*N*D < 2^31 elements.  The selection pass (ba_att_select) and
+ *    ba_att_mask_to_index further need n <= 2048 key blocks per row
+ *    (N <= 131072 at block 64, N <= 262144 at block 128); the diagnostics
+ *    state their own limits.  Shapes beyond a limit return
+ *    BA_ERR_UNSUPPORTED.
  *  - Every pointer argument is a DEVICE pointer on the current HIP device,
  *    16-byte aligned (the mask, idx and cnt buffers 4-byte aligned), owned by
  *    the caller.  The library allocates nothing, keeps no state between
@@ -75,7 +79,8 @@ int32_t ba_att_num_blocks(int32_t N, int32_t block);
 int32_t ba_att_keep_count(int32_t n_blocks, double sparsity);
 
 /* Bytes of device workspace ba_att_select needs: the pooled block statistics
- * of Q and K, 2 * B*H*n * 3*D fp32.  Returns 0 for invalid sizes. */
+ * of Q and K, 2 * B*H*n * 3*D fp32.  Returns 0 for invalid sizes.  (A helper
+ * of this interface; the pages define no workspace.) */
 size_t ba_att_select_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block);
 
 /* Selection pass (review, "What carries the argument": block-wise
@@ -94,18 +99,21 @@ size_t ba_att_select_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D,
  *   block_cnt   int32 [B,H,n], all equal to keep                   (out)
  *   score       fp32 [B,H,n,n] (the map S), or NULL to skip        (out)
  *   workspace   >= ba_att_select_workspace_bytes(...) bytes        (scratch)
- * Supported here: n <= 512 (otherwise BA_ERR_UNSUPPORTED). */
+ * Supported: n <= 2048 (otherwise BA_ERR_UNSUPPORTED). */
 int ba_att_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
                   double sparsity, const void* q, const void* k, uint8_t* block_mask,
                   int32_t* block_idx, int32_t* block_cnt, float* score, void* workspace,
                   size_t workspace_bytes, void* stream);
 
 /* Compacts a block mask into index lists, so a caller's own mask can drive
- * ba_att_forward.  Per row: block_cnt = number of ones; block_idx holds the
- * ascending indices of the first min(cnt, max_keep) ones (a row with more
- * than max_keep ones is truncated, detectable as cnt > max_keep).
+ * ba_att_forward.  (A helper of this interface, not an operation of the
+ * pages: the block mask is their statement of the selection, the index list
+ * is this library's compacted form of it.)  Per row: block_cnt = number of
+ * ones; block_idx holds the ascending indices of the first
+ * min(cnt, max_keep) ones (a row with more than max_keep ones is truncated,
+ * detectable as cnt > max_keep).
  *   block_mask uint8 [B,H,n,n] (in); block_idx int32 [B,H,n,max_keep],
- *   block_cnt int32 [B,H,n] (out).  Supported: n <= 1024. */
+ *   block_cnt int32 [B,H,n] (out).  Supported: n <= 2048. */
 int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* block_mask,
                          int32_t max_keep, int32_t* block_idx, int32_t* block_cnt, void* stream);
 
@@ -232,7 +240,8 @@ int ba_att_score_full(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block,
 int ba_att_rank_agreement(int32_t B, int32_t H, int32_t n_blocks, int32_t keep, const float* x,
                           const float* r, float* recall, float* rho, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code.  (A helper of this interface; not an
+ * operation of the pages.) */
 const char* ba_att_status_string(int status);
 
 #ifdef __cplusplus

@@ -93,7 +93,8 @@ def test_select_rejects_before_launch(lib):
     assert call(N=0) == 1 and call(B=0) == 1
     assert call(D=96) == 2
     assert call(block=32) == 2
-    assert call(N=513 * 64) == 2             # more than 512 blocks per row
+    assert call(N=2049 * 64) == 2            # more than 2048 blocks per row
+    assert call(N=4097 * 128, block=128) == 2
     assert call(q=FAKE + 2) == 1             # misaligned
     assert call(ws=None) == 3
     assert call(wsb=16) == 3
@@ -171,7 +172,7 @@ def test_mask_to_index_rejects_before_launch(lib):
                                         a["cnt"], None)
 
     assert m2i(mask=None) == 1 and m2i(mk=0) == 1 and m2i(n=0) == 1
-    assert m2i(n=1025) == 2
+    assert m2i(n=2049) == 2
     assert m2i(idx=FAKE + 1) == 1
 
 
@@ -262,3 +263,4 @@ def test_split_parts_rejects_invalid_shapes_before_any_device_query(lib):
     assert lib.ba_att_forward_split_parts(1, 1, 1024, 96, 4) == 0
     assert lib.ba_att_forward_split_parts(1, 1, 1024, 64, 0) == 0
     assert lib.ba_att_forward_split_parts(1, 1, (1 << 20) + 1, 64, 4) == 0
+

@@ -12,12 +12,19 @@ from block_sparse_attention_ba_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def test_select_forward_graph_replays_match_eager(gpu_lib):
+# the second shape gives the score pass 64 rows per workgroup and 115 KB of
+# LDS, so its launch also sets the kernel's dynamic-LDS attribute under capture
+SHAPES = [(1, 4, 3000, 128, 64, 0.5), (1, 64, 16384, 128, 64, 0.5)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["small", "wide-score-tiles"])
+def test_select_forward_graph_replays_match_eager(gpu_lib, shape):
     import torch
     from block_sparse_attention_ba_amd import _lib
 
     lib = _lib.load()
-    B, H, N, D, blk, sp = 1, 4, 3000, 128, 64, 0.5
+    B, H, N, D, blk, sp = shape
+    print("graph capture case", shape, flush=True)
     dev = torch.device("cuda:0")
 
     def bits(seed):

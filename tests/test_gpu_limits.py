@@ -1,8 +1,11 @@
 """The operator at the edges of its supported sizes, against the fp64 oracle
 through the C ABI:
 
-* selection at the longest supported rows (n = 512 key blocks), masks
-  bit-exact except near-tie rows;
+* selection at long rows up to the longest supported (n = 512, 1024 and
+  2048 key blocks, one head, and with enough heads that the score pass
+  takes 32 query-block rows per workgroup), masks bit-exact except near-tie
+  rows, index lists the ascending ones of the mask, and the score map
+  within an fp32 bound of the oracle's;
 * the block-sparse forward at N = 2^18 with a ragged tail block, and at the
   ABI's largest sequence N = 2^20, each from a host-built block list (a few
   random blocks per row, the partial tail block, an empty row), on sampled
@@ -18,7 +21,7 @@ import pytest
 
 from block_sparse_attention_ba_amd import workloads as wl
 from oracle import ba_att_oracle as orc
-from tests.helpers import LSE_TOL, O_TOL, compare_masks, max_abs, to_dev
+from tests.helpers import LSE_TOL, O_TOL, compare_masks, index_matches_mask, max_abs, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -32,25 +35,41 @@ def rand_bits(shape, seed):
     return wl.f32_to_bf16_bits(x)
 
 
-@pytest.mark.parametrize("N,D,block", [(32768, 64, 64), (65536, 128, 128)])
-def test_select_at_longest_rows(gpu_lib, N, D, block):
+SELECT_CASES = [(1, 32768, 64, 64), (1, 65536, 128, 128), (16, 65536, 128, 128),
+                (1, 131072, 128, 128), (8, 131072, 128, 128), (1, 131072, 128, 64), (1, 131071, 64, 64)]
+
+
+@pytest.mark.parametrize("H,N,D,block", SELECT_CASES, ids=[f"H{c[0]}-N{c[1]}-D{c[2]}-b{c[3]}" for c in SELECT_CASES])
+def test_select_at_long_rows(gpu_lib, H, N, D, block):
     import torch
     n = orc.num_blocks(N, block)
-    assert n == 512
-    _log("select limits case", (N, D, block))
-    rng = np.random.default_rng(N)
-    # clustered rows so that the 256 kept blocks of a row have clear winners
-    mu = rng.standard_normal((16, D)).astype(np.float32)
-    lab = rng.integers(0, 16, size=N // 64).repeat(64)[:N]
-    q = wl.f32_to_bf16_bits(mu[lab] + 0.5 * rng.standard_normal((N, D)).astype(np.float32))[None, None]
-    k = wl.f32_to_bf16_bits(mu[lab] + 0.5 * rng.standard_normal((N, D)).astype(np.float32))[None, None]
-    mask, idx, cnt = gpu_lib.select(to_dev(q), to_dev(k), block, 0.5)
+    assert n in (512, 1024, 2048)
+    _log("select limits case", (H, N, D, block), "n", n)
+    rng = np.random.default_rng(N + H)
+    # clustered rows so that the kept half of a row has clear winners
+    q = np.empty((1, H, N, D), np.uint16)
+    k = np.empty((1, H, N, D), np.uint16)
+    for h in range(H):
+        mu = rng.standard_normal((16, D)).astype(np.float32)
+        lab = rng.integers(0, 16, size=N // 64 + 1).repeat(64)[:N]
+        q[0, h] = wl.f32_to_bf16_bits(mu[lab] + 0.5 * rng.standard_normal((N, D)).astype(np.float32))
+        k[0, h] = wl.f32_to_bf16_bits(mu[lab] + 0.5 * rng.standard_normal((N, D)).astype(np.float32))
+    mask, idx, cnt, score = gpu_lib.select(to_dev(q), to_dev(k), block, 0.5, return_score=True)
     torch.cuda.synchronize()
     ref = orc.select_oracle(q, k, block, 0.5)
-    res = compare_masks(mask.cpu().numpy(), ref["S"], ref["mask"], ref["keep"])
+    gm = mask.cpu().numpy()
+    res = compare_masks(gm, ref["S"], ref["mask"], ref["keep"])
     _log("select limits", {k2: v2 for k2, v2 in res.items() if k2 != "bad"})
     assert not res["bad"], res["bad"][:5]
     assert np.all(cnt.cpu().numpy() == ref["keep"])
+    assert index_matches_mask(gm, idx.cpu().numpy(), cnt.cpu().numpy())
+    # |dS| within a few fp32 ulps of the sum of the absolute terms
+    s = ref["scale"]
+    hs2 = 0.5 * s * s
+    terms = (s * np.abs(ref["qm"]) @ np.abs(ref["km"]).transpose(0, 1, 3, 2)
+             + hs2 * (ref["qv"] @ (ref["kv"] + ref["km"] ** 2).transpose(0, 1, 3, 2)
+                      + ref["qm"] ** 2 @ ref["kv"].transpose(0, 1, 3, 2)))
+    assert np.all(np.abs(score.cpu().numpy() - ref["S"]) <= 4e-5 * terms + 1e-7)
 
 
 def host_lists(n, keep, rng):
