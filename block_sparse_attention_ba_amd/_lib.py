@@ -19,6 +19,8 @@ SIGNATURES = [
     ("ba_att_select_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
     ("ba_att_select", ctypes.c_int,
      [_i32, _i32, _i32, _i32, _i32, _f32, _f64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    ("ba_att_select_noalloc", ctypes.c_int,
+     [_i32, _i32, _i32, _i32, _i32, _f32, _f64, _p, _p, _p, _p, _p, _p, _p]),
     ("ba_att_mask_to_index", ctypes.c_int, [_i32, _i32, _i32, _p, _i32, _p, _p, _p]),
     ("ba_att_forward", ctypes.c_int,
      [_i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p]),

@@ -16,7 +16,7 @@ from . import _lib
 BA_BF16, BA_F32 = 0, 1
 
 __all__ = [
-    "load", "num_blocks", "keep_count", "select_workspace_bytes", "select", "mask_to_index",
+    "load", "num_blocks", "keep_count", "select_workspace_bytes", "select", "select_noalloc", "mask_to_index",
     "forward", "forward_split", "forward_split_workspace_bytes", "forward_split_parts", "forward_auto",
     "merge", "forward_ext", "dense",
     "ba_attention", "block_map", "score_full_workspace_bytes", "score_full", "rank_agreement",
@@ -109,6 +109,44 @@ def select(q: torch.Tensor, k: torch.Tensor, block: int, sparsity: float, scale:
                                  q.data_ptr(), k.data_ptr(), mask.data_ptr(), idx.data_ptr(),
                                  cnt.data_ptr(), score.data_ptr() if score is not None else None,
                                  workspace.data_ptr(), ws_bytes, _stream(q)))
+    if return_score:
+        return mask, idx, cnt, score
+    return mask, idx, cnt
+
+
+def select_noalloc(q: torch.Tensor, k: torch.Tensor, block: int, sparsity: float, scale: float | None = None,
+                   return_score: bool = False, out=None):
+    """ba_att_select_noalloc: the selection pass with the library's fixed
+    device scratch instead of a workspace.  `out` = (mask, idx, cnt) lets a
+    caller that cannot allocate pass its own outputs (shapes as returned by
+    select); otherwise they are allocated here."""
+    B, H, N, D = _qkv_shape(q)
+    _need(k, "k", torch.bfloat16, 4, q.device)
+    if tuple(k.shape) != (B, H, N, D):
+        raise ValueError("q and k must have the same shape")
+    lib = _lib.load()
+    n = num_blocks(N, block)
+    keep = keep_count(n, sparsity)
+    if keep < 1:
+        raise ValueError("sparsity must lie in [0, 1)")
+    dev = q.device
+    if out is None:
+        mask = torch.empty((B, H, n, n), dtype=torch.uint8, device=dev)
+        idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    else:
+        mask, idx, cnt = out
+        for t, name, dt, shape in ((mask, "mask", torch.uint8, (B, H, n, n)), (idx, "idx", torch.int32, (B, H, n, keep)),
+                                   (cnt, "cnt", torch.int32, (B, H, n))):
+            _need(t, name, dt, None, dev)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}")
+    score = torch.empty((B, H, n, n), dtype=torch.float32, device=dev) if return_score else None
+    with _on(q):
+        _check(lib.ba_att_select_noalloc(B, H, N, D, block, float(scale or 0.0), float(sparsity),
+                                         q.data_ptr(), k.data_ptr(), mask.data_ptr(), idx.data_ptr(),
+                                         cnt.data_ptr(), score.data_ptr() if score is not None else None,
+                                         _stream(q)))
     if return_score:
         return mask, idx, cnt, score
     return mask, idx, cnt

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 
 #include "ba_att.h"
@@ -198,6 +199,55 @@ int ba_att_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, flo
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return BA_ERR_WORKSPACE;
   return launch_select(B, H, N, D, block, scale, sparsity, q, k, block_mask, block_idx, block_cnt, score,
                        static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------- no-allocation
+// Fixed device scratch of ba_att_select_noalloc: the pooled statistics of
+// the selection pass for callers that cannot allocate.  One copy per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in): it uses the
+// per-device address from hipGetSymbolAddress.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// Address of the current device's scratch, looked up once per device.
+ba_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int ba_att_select_noalloc(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                          double sparsity, const void* q, const void* k, uint8_t* block_mask,
+                          int32_t* block_idx, int32_t* block_cnt, float* score, void* stream) {
+  ba_status st = check_select(B, H, N, D, block, sparsity, q, k, block_mask, block_idx, block_cnt, score);
+  if (st != BA_OK) return st;
+  if (ba_att_select_workspace_bytes(B, H, N, D, block) > kScratchBytes) return BA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != BA_OK) return st;
+  return launch_select(B, H, N, D, block, scale, sparsity, q, k, block_mask, block_idx, block_cnt, score,
+                       static_cast<float*>(ws), static_cast<hipStream_t>(stream));
 }
 
 int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* block_mask,
@@ -576,6 +626,7 @@ const char* ba_att_status_string(int status) {
     case BA_ERR_UNSUPPORTED: return "unsupported shape or size";
     case BA_ERR_WORKSPACE: return "workspace missing or too small";
     case BA_ERR_HIP: return "HIP launch failed";
+    case BA_ERR_SCRATCH: return "shape needs more than the 64 MiB fixed scratch of ba_att_select_noalloc";
     default: return "unknown status";
   }
 }

@@ -62,7 +62,8 @@ typedef enum {
   BA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, sparsity outside [0,1), misalignment */
   BA_ERR_UNSUPPORTED = 2, /* D or block outside the supported set, sizes too large */
   BA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ba_att_select_workspace_bytes */
-  BA_ERR_HIP = 4          /* a HIP launch failed */
+  BA_ERR_HIP = 4,         /* a HIP launch failed */
+  BA_ERR_SCRATCH = 5      /* ba_att_select_noalloc: the shape needs more than its fixed scratch */
 } ba_status;
 
 typedef enum { BA_BF16 = 0, BA_F32 = 1 } ba_dtype;
@@ -104,6 +105,23 @@ int ba_att_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, flo
                   double sparsity, const void* q, const void* k, uint8_t* block_mask,
                   int32_t* block_idx, int32_t* block_cnt, float* score, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* ba_att_select without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus the workspace),
+ * checks and results as ba_att_select, bit for bit.  The pooled statistics
+ * go to a fixed scratch array in the library's device code: 64 MiB per GPU,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends.  A shape whose ba_att_select_workspace_bytes exceeds
+ * 64 MiB (67108864 bytes) returns BA_ERR_SCRATCH and launches nothing.  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (concurrent streams, or host threads on the
+ * same device) race and must be serialised by the caller; consecutive calls
+ * on one stream are safe, since each call writes every scratch entry it
+ * reads. */
+int ba_att_select_noalloc(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                          double sparsity, const void* q, const void* k, uint8_t* block_mask,
+                          int32_t* block_idx, int32_t* block_cnt, float* score, void* stream);
 
 /* Compacts a block mask into index lists, so a caller's own mask can drive
  * ba_att_forward.  (A helper of this interface, not an operation of the

@@ -264,3 +264,24 @@ def test_split_parts_rejects_invalid_shapes_before_any_device_query(lib):
     assert lib.ba_att_forward_split_parts(1, 1, 1024, 64, 0) == 0
     assert lib.ba_att_forward_split_parts(1, 1, (1 << 20) + 1, 64, 4) == 0
 
+
+def test_select_noalloc_rejects_before_launch(lib):
+    """The allocation-free selection call checks its arguments like
+    ba_att_select and refuses, before touching the GPU, a shape whose pooled
+    statistics exceed its fixed 64 MiB scratch."""
+    ok = dict(B=1, H=1, N=1024, D=64, block=64, scale=0.0, sp=0.5)
+
+    def call(**kw):
+        a = dict(ok, q=FAKE, k=FAKE, mask=FAKE, idx=FAKE, cnt=FAKE, score=None)
+        a.update(kw)
+        return lib.ba_att_select_noalloc(a["B"], a["H"], a["N"], a["D"], a["block"], a["scale"], a["sp"],
+                                         a["q"], a["k"], a["mask"], a["idx"], a["cnt"], a["score"], None)
+
+    assert call(q=None) == 1 and call(sp=1.0) == 1 and call(q=FAKE + 2) == 1
+    assert call(D=96) == 2 and call(block=32) == 2 and call(N=2049 * 64) == 2
+    # 2*64*1024*384*4 bytes of statistics: beyond the scratch
+    assert lib.ba_att_select_workspace_bytes(2, 32, 65536, 128, 64) > (64 << 20)
+    assert call(B=2, H=32, N=65536, D=128, block=64) == 5
+    # the distribution-shift shape (B2 H32 N32768 D128 b128) fits: 48 MiB
+    assert lib.ba_att_select_workspace_bytes(2, 32, 32768, 128, 128) == 48 << 20
+    assert b"scratch" in lib.ba_att_status_string(5)
