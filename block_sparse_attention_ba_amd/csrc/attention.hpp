@@ -31,6 +31,13 @@
 //    the wave finds a new maximum (a wave-uniform branch).
 //  * The sparse variant walks the compacted block-index list of its query
 //    block; the dense variant walks all keys.  Keys >= N are masked to -inf.
+//  * The sparse walk visits a row's kept blocks in one order shared by every
+//    row (increasing (J * g) mod n, g near n/phi): each kept set is spread
+//    evenly over that order, so the walks of the workgroups resident on an
+//    XCD advance together and read each shared key block from L2 at about
+//    the same time.  Ascending walks would not: kept blocks cluster around
+//    each row's own diagonal band and key runs, so concurrent rows sit at
+//    different keys.
 #pragma once
 
 #include "common.hpp"
@@ -61,7 +68,14 @@ struct AttnParams {
   // over another key set, merged into the result in log space
   const float* o_ext;
   const float* lse_ext;
+  // sparse walk order: a row's kept blocks are visited in increasing
+  // (J * walk_mul) mod n_blocks, one order shared by every row of every head
+  // (0: the list's own order)
+  int walk_mul;
 };
+
+// Longest block list a workgroup reorders (longer lists are walked as given).
+constexpr int kMaxOrdered = 1024;
 
 constexpr int kChunk = 64;  // keys per LDS chunk
 
@@ -94,6 +108,15 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A wave-uniform int32 read through the scalar cache.  The load is written
+// out, with its wait, so that the compiler neither treats the (written)
+// memory as constant nor lets the read move above the writes before it.
+__device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
+  int v;
+  __asm__ volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
 }
 
 // Copy j of a 64-key tile: lane `lane` of wave `wave` fills LDS slot
@@ -144,23 +167,77 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   const uint16_t* Kh = p.k + head;
   const uint16_t* Vh = p.v + head;
 
-  // ---- chunk schedule; the block lists are read through the constant
-  // address space (scalar loads, which never wait for the tile copies)
-  typedef const __attribute__((address_space(4))) int32_t* cidx_t;
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once; in flight
+  // while the block list is reordered
+  const int qrow = qt * ROWS + wave * 32 + lq;
+  bf16x8 qf[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (qrow < N) w = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + ks * 16 + g * 8);
+    qf[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+
+  // ---- chunk schedule: block-list entries are read with scalar loads
+  // (which never wait for the tile copies)
   int n_chunks;
-  cidx_t idx_row = nullptr;
+  const int32_t* list = nullptr;
   if constexpr (SPARSE) {
+    typedef const __attribute__((address_space(4))) int32_t* cidx_t;
     const int row = bh * p.n_blocks + qt;
     int c = ((cidx_t)p.cnt)[row];
     c = c < 0 ? 0 : (c > p.max_keep ? p.max_keep : c);
     n_chunks = c * SUBS;
-    idx_row = (cidx_t)p.idx + (size_t)row * p.max_keep;
+    list = p.idx + (size_t)row * p.max_keep;
+    // Walk order.  The kept blocks of one row cluster (a band around the
+    // diagonal, runs of similar keys), so ascending walks of the rows that
+    // are resident together sit at different keys at any moment and share
+    // little of L2.  In the order of increasing (J * walk_mul) mod n -- a
+    // golden-ratio stride, the same for every row -- any kept set is spread
+    // evenly, so the walks advance together and a block kept by many rows is
+    // read by all of them at about the same time.  The list is reordered by a
+    // rank sort of packed (key, J) words (repeated entries stay; entries
+    // outside [0, n) sort last) and stored in this workgroup's own output
+    // rows, which hold nothing else until the epilogue: every wave passes two
+    // barriers after its last list read before any output is written.  A
+    // full list (c = n) keeps its order, which is then the dense walk; a list
+    // longer than kMaxOrdered, or than the output rows hold, is walked as
+    // given.
+    const size_t out_elem = OUT_F32 ? 4 : 2;
+    const int rows_here = min(ROWS, N - qt * ROWS);
+    const bool ordered = p.walk_mul > 0 && c > 1 && c <= kMaxOrdered && c < p.n_blocks &&
+                         (size_t)c * 4 <= (size_t)rows_here * D * out_elem;
+    if (ordered) {
+      uint32_t* const keys = reinterpret_cast<uint32_t*>(Vtile);  // free until the first copy of V
+      static_assert(TILE_BYTES >= kMaxOrdered * 4, "V tile holds the keys");
+      int32_t* const out = reinterpret_cast<int32_t*>(
+          reinterpret_cast<uint8_t*>(p.o) +
+          (part * p.o_part_stride + ((size_t)bh * N + (size_t)qt * ROWS) * D) * out_elem);
+      const int n = p.n_blocks;
+      for (int e = threadIdx.x; e < c; e += WAVES * 64) {
+        const int J = list[e];
+        keys[e] = (J >= 0 && J < n) ? ((uint32_t)((J * p.walk_mul) % n) << 16) | (uint32_t)J : 0xFFFFFFFFu;
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < c; e += WAVES * 64) {
+        const uint32_t v = keys[e];
+        int rank = 0;
+        for (int j = 0; j < c; ++j) {
+          const uint32_t w = keys[j];
+          rank += (w < v) || (w == v && j < e);
+        }
+        out[rank] = v == 0xFFFFFFFFu ? -1 : (int32_t)(v & 0xFFFFu);
+      }
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the list is in L2
+      __syncthreads();
+      list = out;
+    }
   } else {
     n_chunks = (N + kChunk - 1) / kChunk;
   }
   auto chunk_start = [&](int c) -> int {  // first key of chunk c, or -1 if skipped
     if constexpr (SPARSE) {
-      const int J = idx_row[c / SUBS];
+      const int J = scalar_load_i32(list + c / SUBS);
       if (J < 0 || J >= p.n_blocks) return -1;
       return J * BLK + (c % SUBS) * kChunk;
     } else {
@@ -191,16 +268,6 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int first = __builtin_amdgcn_readfirstlane(k0 < 0 ? 0 : k0);
     return make_rsrc(src + (size_t)first * D, rows * ROW_BYTES);
   };
-
-  // ---- Q fragments (B operand of S^T = K Q^T), loaded once
-  const int qrow = qt * ROWS + wave * 32 + lq;
-  bf16x8 qf[KSTEPS];
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (qrow < N) w = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + ks * 16 + g * 8);
-    qf[ks] = __builtin_bit_cast(bf16x8, w);
-  }
 
   // ---- LDS operand reads
   auto read_k = [&](int kt, int ks) -> bf16x8 {  // A of S^T: key kt*32+lq, d = 16ks+8g..+8

@@ -277,6 +277,20 @@ namespace {
 
 constexpr int kMaxSplit = 64;
 
+// Multiplier of the sparse walk order: the integer nearest n/phi (phi the
+// golden ratio) that is coprime with n, so that J -> J*g mod n permutes the
+// blocks and scatters neighbouring blocks across the walk.
+int walk_multiplier(int n) {
+  if (n <= 2) return 1;
+  auto gcd = [](int a, int b) { while (b) { const int t = a % b; a = b; b = t; } return a; };
+  const int g0 = (int)lround(n * 0.6180339887498949);
+  for (int d = 0; d < n; ++d) {
+    if (g0 - d >= 1 && gcd(g0 - d, n) == 1) return g0 - d;
+    if (g0 + d < n && gcd(g0 + d, n) == 1) return g0 + d;
+  }
+  return 1;
+}
+
 // Checks of the arguments every forward variant shares.
 ba_status check_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, const void* q,
                         const void* k, const void* v, const int32_t* block_idx, const int32_t* block_cnt,
@@ -323,6 +337,7 @@ ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t blo
   p.lse_part_stride = lse_stride;
   p.o_ext = o_ext;
   p.lse_ext = lse_ext;
+  p.walk_mul = walk_multiplier(n);
   if (D == 128) {
     if (block == 64) launch_attn<128, 2, 64, true>(p, o_f32, s);
     else launch_attn<128, 4, 128, true>(p, o_f32, s);

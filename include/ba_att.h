@@ -142,7 +142,11 @@ int ba_att_mask_to_index(int32_t B, int32_t H, int32_t n_blocks, const uint8_t* 
  *   LSE_s = ln sum_t exp(scale*<q_s,k_t>),  O_s = sum_t exp(scale*<q_s,k_t> - LSE_s) v_t.
  * Entries outside [0, n) are skipped; entries must be distinct (a repeated
  * entry is counted twice).  A row with no valid entry gives O = 0 and
- * LSE = -inf.
+ * LSE = -inf.  The entries may come in any order: the kernel visits them in
+ * an order of its own (one shared by every row), so results equal the
+ * oracle's up to fp32 rounding order.  o must not overlap any input: the
+ * kernel keeps its reordered list in a row's own output rows until it
+ * writes them.
  *   q, k, v  bf16 [B,H,N,D] (in); block_idx/block_cnt as above (in);
  *   o        [B,H,N,D] of o_dtype (BA_BF16 or BA_F32) (out);
  *   lse      fp32 [B,H,N] natural log including the scale, or NULL (out). */
