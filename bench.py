@@ -79,8 +79,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for traffic counters)")
     ap.add_argument("--power", action="store_true",
-                    help="also sample socket power and graphics clocks (amd-smi) while the sparse and the "
-                         "dense kernel each run back to back for a few seconds")
+                    help="also sample socket power and graphics clocks (amd-smi) while the sparse kernel, "
+                         "the dense kernel and the bf16 MFMA peak loop each run back to back for a few seconds")
     ap.add_argument("--skip-split", action="store_true",
                     help="omit the split key-list and external-contribution measurements")
     ap.add_argument("--skip-sweep", action="store_true",
@@ -405,6 +405,25 @@ def power_sample(run, stream, seconds: float) -> dict:
     return {"mean_ms_per_call": round(ms, 5), "samples": samples}
 
 
+def mfma_loop_power(dev, stream, seconds: float) -> dict:
+    """Socket power and clocks while the bf16 MFMA peak loop (libba_peaks.so:
+    2 waves per SIMD, 4 independent MFMA chains, no memory traffic) runs back
+    to back: what the matrix pipes alone draw at full rate."""
+    import torch
+    from block_sparse_attention_ba_amd import _lib
+    pk = _lib.load_peaks()
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(n_cu * 2 * 256, dtype=torch.float32, device=dev)
+
+    def run():
+        if pk.ba_peak_mfma_bf16(sink.data_ptr(), n_cu * 2, 20000, 2.0 ** -10, stream.cuda_stream) != 0:
+            raise RuntimeError("peak microbenchmark launch failed")
+
+    res = power_sample(run, stream, seconds)
+    res["tflops"] = round(n_cu * 2 * 4 * 20000 * 4 * 32768 / (res["mean_ms_per_call"] * 1e-3) / 1e12, 1)
+    return res
+
+
 def measured_peaks(dev, stream, reps: int = 5) -> dict:
     """HBM read and copy bandwidth and the bf16 MFMA rate measured on this GPU
     (libba_peaks.so), as context for the vendor peaks the rooflines use."""
@@ -703,7 +722,8 @@ def main():
 
     power = None
     if args.power:
-        power = {"sparse": power_sample(P.sparse, stream, 4.0), "dense": power_sample(P.dense, stream, 4.0)}
+        power = {"sparse": power_sample(P.sparse, stream, 4.0), "dense": power_sample(P.dense, stream, 4.0),
+                 "mfma_loop": mfma_loop_power(dev, stream, 4.0)}
         print(f"[bench] power: {power}", file=sys.stderr, flush=True)
 
     # ---- the product path's own outputs for the parity check against the
