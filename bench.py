@@ -92,7 +92,7 @@ def parse():
 
 def split_kv_measurement(lib, dev, stream, warmup: int, reps: int) -> dict:
     """Split key lists on a shape whose workgroups half-fill the device:
-    one head, N = 32768, D = 128, block 64 (512 query blocks of 2 waves) at
+    one head, N = 32768, D = 128, block 64 (512 query blocks in 256 four-wave tiles) at
     50% sparsity.  Times ba_att_forward against ba_att_forward_split."""
     import numpy as np
     import torch

@@ -140,7 +140,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int TILE_BYTES = kChunk * ROW_BYTES;
   constexpr int DMA = (kChunk * CPR) / (64 * WAVES);  // 16-byte loads per lane per tile
   constexpr int SUBS = SPARSE ? BLK / kChunk : 1;     // chunks per listed block
-  static_assert(!SPARSE || ROWS == BLK, "sparse tile must be one query block");
+  // a sparse tile is one query block, or (PAIR) two neighbouring ones
+  constexpr bool PAIR = SPARSE && ROWS == 2 * BLK;
+  static_assert(!SPARSE || ROWS == BLK || PAIR, "sparse tile must be one or two query blocks");
   static_assert((kChunk * CPR) % (64 * WAVES) == 0, "tile must split evenly over the waves");
 
   // two separate arrays: the compiler then sees that a copy into one does not
@@ -181,66 +183,137 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   // ---- chunk schedule: block-list entries are read with scalar loads
   // (which never wait for the tile copies)
   int n_chunks;
-  const int32_t* list = nullptr;
+  const int32_t* listA = nullptr;  // caller's list of the (first) query block
+  const int32_t* listB = nullptr;  // caller's list of the second block of a pair
+  const int32_t* walk = nullptr;   // a built walk: (owner bits << 16) | J per entry
+  int cA = 0;
+  int my_bit = 1;                  // owner bit of this wave's query block
   if constexpr (SPARSE) {
     typedef const __attribute__((address_space(4))) int32_t* cidx_t;
-    const int row = bh * p.n_blocks + qt;
-    int c = ((cidx_t)p.cnt)[row];
-    c = c < 0 ? 0 : (c > p.max_keep ? p.max_keep : c);
-    n_chunks = c * SUBS;
-    list = p.idx + (size_t)row * p.max_keep;
+    const int n = p.n_blocks;
+    const int qb = PAIR ? 2 * qt : qt;
+    const int rowA = bh * n + qb;
+    auto clamp_cnt = [&](int c) { return c < 0 ? 0 : (c > p.max_keep ? p.max_keep : c); };
+    cA = clamp_cnt(((cidx_t)p.cnt)[rowA]);
+    listA = p.idx + (size_t)rowA * p.max_keep;
+    int cB = 0;
+    if constexpr (PAIR) {
+      my_bit = wave < WAVES / 2 ? 1 : 2;
+      if (qb + 1 < n) {
+        cB = clamp_cnt(((cidx_t)p.cnt)[rowA + 1]);
+        listB = listA + p.max_keep;
+      }
+    }
+    const int tot = cA + cB;
+    n_chunks = tot * SUBS;  // as given: the first block's entries, then the second's
     // Walk order.  The kept blocks of one row cluster (a band around the
     // diagonal, runs of similar keys), so ascending walks of the rows that
     // are resident together sit at different keys at any moment and share
     // little of L2.  In the order of increasing (J * walk_mul) mod n -- a
     // golden-ratio stride, the same for every row -- any kept set is spread
     // evenly, so the walks advance together and a block kept by many rows is
-    // read by all of them at about the same time.  The list is reordered by a
-    // rank sort of packed (key, J) words (repeated entries stay; entries
-    // outside [0, n) sort last) and stored in this workgroup's own output
-    // rows, which hold nothing else until the epilogue: every wave passes two
-    // barriers after its last list read before any output is written.  A
-    // full list (c = n) keeps its order, which is then the dense walk; a list
-    // longer than kMaxOrdered, or than the output rows hold, is walked as
-    // given.
+    // read by all of them at about the same time.  A pair of query blocks
+    // walks the union of its two lists in that order, each entry tagged with
+    // the blocks that keep it, so a block both keep is copied to LDS once.
+    //
+    // The walk is built by a stable rank sort of packed words
+    // (key << 16 | J << 1 | list), so an entry of the second list follows
+    // the equal entry of the first, and merging each such pair into one
+    // entry keeps repeated entries' multiplicity; entries outside [0, n)
+    // sort last.  It is stored in this tile's own output rows, which hold
+    // nothing else until the epilogue: every wave passes two barriers after
+    // its last walk read before any output is written.  Full lists keep
+    // ascending order (then the walk equals the dense one); a walk longer
+    // than 2*kMaxOrdered, or than the output rows hold, is taken as given.
     const size_t out_elem = OUT_F32 ? 4 : 2;
     const int rows_here = min(ROWS, N - qt * ROWS);
-    const bool ordered = p.walk_mul > 0 && c > 1 && c <= kMaxOrdered && c < p.n_blocks &&
-                         (size_t)c * 4 <= (size_t)rows_here * D * out_elem;
-    if (ordered) {
-      uint32_t* const keys = reinterpret_cast<uint32_t*>(Vtile);  // free until the first copy of V
-      static_assert(TILE_BYTES >= kMaxOrdered * 4, "V tile holds the keys");
+    const bool full = cA == n && (!PAIR || qb + 1 >= n || cB == n);
+    const bool build = p.walk_mul > 0 && tot > 1 && tot <= 2 * kMaxOrdered &&
+                       (size_t)tot * 4 <= (size_t)rows_here * D * out_elem && (PAIR || !full);
+    if (build) {
+      constexpr int T = WAVES * 64;
+      static_assert(TILE_BYTES >= 2 * kMaxOrdered * 4, "a tile holds the packed walk");
+      // K and V tiles are free until their first copies
+      uint32_t* const keys = reinterpret_cast<uint32_t*>(Vtile);
+      uint32_t* const sorted = reinterpret_cast<uint32_t*>(Ktile);
+      int* const scan = reinterpret_cast<int*>(Vtile);  // reused once the keys are ranked
       int32_t* const out = reinterpret_cast<int32_t*>(
           reinterpret_cast<uint8_t*>(p.o) +
           (part * p.o_part_stride + ((size_t)bh * N + (size_t)qt * ROWS) * D) * out_elem);
-      const int n = p.n_blocks;
-      for (int e = threadIdx.x; e < c; e += WAVES * 64) {
-        const int J = list[e];
-        keys[e] = (J >= 0 && J < n) ? ((uint32_t)((J * p.walk_mul) % n) << 16) | (uint32_t)J : 0xFFFFFFFFu;
+      for (int e = threadIdx.x; e < tot; e += T) {
+        const bool inB = e >= cA;
+        const int J = inB ? listB[e - cA] : listA[e];
+        const uint32_t own = inB ? 1u : 0u;
+        const uint32_t key = full ? (uint32_t)J : (uint32_t)((J * p.walk_mul) % n);
+        keys[e] = (J >= 0 && J < n) ? (key << 16) | ((uint32_t)J << 1) | own : (0xFFFFFFFEu | own);
       }
       __syncthreads();
-      for (int e = threadIdx.x; e < c; e += WAVES * 64) {
+      for (int e = threadIdx.x; e < tot; e += T) {
         const uint32_t v = keys[e];
         int rank = 0;
-        for (int j = 0; j < c; ++j) {
+        for (int j = 0; j < tot; ++j) {
           const uint32_t w = keys[j];
           rank += (w < v) || (w == v && j < e);
         }
-        out[rank] = v == 0xFFFFFFFFu ? -1 : (int32_t)(v & 0xFFFFu);
+        sorted[rank] = v;
       }
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the list is in L2
       __syncthreads();
-      list = out;
+      // an entry of the second list merges into an equal entry of the first
+      // just before it; every other sorted entry starts a walk entry
+      auto starts = [&](int r) -> bool {
+        if (r == 0) return true;
+        const uint32_t v = sorted[r], u = sorted[r - 1];
+        return !((v >> 1) == (u >> 1) && (v & 1u) && !(u & 1u));
+      };
+      const int seg = (tot + T - 1) / T;
+      const int s0 = min(tot, (int)threadIdx.x * seg), s1 = min(tot, s0 + seg);
+      int mine_starts = 0;
+      for (int r = s0; r < s1; ++r) mine_starts += starts(r);
+      scan[threadIdx.x] = mine_starts;
+      __syncthreads();
+      for (int off = 1; off < T; off <<= 1) {  // inclusive scan of the per-thread counts
+        const int add = (int)threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+        __syncthreads();
+        scan[threadIdx.x] += add;
+        __syncthreads();
+      }
+      int pos = scan[threadIdx.x] - mine_starts;
+      const int walk_len = scan[T - 1];
+      for (int r = s0; r < s1; ++r) {
+        if (!starts(r)) continue;
+        const uint32_t v = sorted[r];
+        uint32_t own_bits = 1u << (v & 1u);
+        if (r + 1 < tot && !starts(r + 1)) own_bits |= 2u;
+        out[pos++] = (int32_t)((own_bits << 16) | ((v >> 1) & 0x7FFFu));
+      }
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the walk is in L2
+      __syncthreads();
+      n_chunks = __builtin_amdgcn_readfirstlane(walk_len) * SUBS;
+      walk = out;
     }
   } else {
     n_chunks = (N + kChunk - 1) / kChunk;
   }
-  auto chunk_start = [&](int c) -> int {  // first key of chunk c, or -1 if skipped
+  // first key of chunk c (-1: skipped) and the owner bits of its block
+  auto chunk_entry = [&](int c, int& own) -> int {
     if constexpr (SPARSE) {
-      const int J = scalar_load_i32(list + c / SUBS);
+      const int i = c / SUBS;
+      int J;
+      if (walk != nullptr) {
+        const int raw = scalar_load_i32(walk + i);
+        J = raw & 0xFFFF;
+        own = raw >> 16;
+      } else if (i < cA) {
+        J = scalar_load_i32(listA + i);
+        own = 1;
+      } else {
+        J = scalar_load_i32(listB + (i - cA));
+        own = 2;
+      }
       if (J < 0 || J >= p.n_blocks) return -1;
       return J * BLK + (c % SUBS) * kChunk;
     } else {
+      own = 3;
       return c * kChunk;
     }
   };
@@ -304,18 +377,24 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   const int c_begin = min(n_chunks, part * per_part);
   const int c_end = min(n_chunks, c_begin + per_part);
 
-  int k0_next = c_begin < c_end ? chunk_start(c_begin) : 0;
+  int own_next = 0;
+  int k0_next = c_begin < c_end ? chunk_entry(c_begin, own_next) : 0;
   if (c_begin < c_end) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
 
   for (int c = c_begin; c < c_end; ++c) {
     const int k0 = k0_next;
+    // in a pair, a wave works only on the blocks its own query block keeps;
+    // it still copies its share of every tile and meets every barrier
+    const bool mine = !PAIR || (own_next & my_bit) != 0;
     const int valid = k0 < 0 ? 0 : max(0, min(kChunk, N - k0));
-    if (c + 1 < c_end) k0_next = chunk_start(c + 1);
+    if (c + 1 < c_end) k0_next = chunk_entry(c + 1, own_next);
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(c) landed
     __syncthreads();  // K(c) visible to all waves; every wave is done with V(c-1)
     dma_tile<DMA, WAVES>(tile_rsrc(Vh, k0), Vbuf, wave, voff_v);
 
+    bf16x8 pf[4];  // P^T operand of each 16-key step
+    if (mine) {
     // S^T (64 keys x 32 queries) = K Q^T, K operands read one k-step ahead
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     bf16x8 kcur[2] = {read_k(0, 0), read_k(1, 0)};
@@ -366,7 +445,6 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
     float psum = 0.f;
-    bf16x8 pf[4];  // P^T operand of each 16-key step
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -390,11 +468,13 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     // PV MFMAs and the copy of K(c+1) starts earlier.
     if constexpr (WAVES == 4)
       __asm__ volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l_run));
+    }
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(c) landed
     __syncthreads();  // V(c) visible; every wave is done with K(c)
     if (c + 1 < c_end) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
 
+    if (!mine) continue;
     // O^T (D x 32 queries) += V^T P^T, V operands read one step ahead
     bf16x8 vcur[DT];
 #pragma unroll

@@ -316,7 +316,10 @@ ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t blo
                          float* lse, size_t o_stride, size_t lse_stride, const float* o_ext,
                          const float* lse_ext, hipStream_t s) {
   const int n = num_blocks(N, block);
-  const long long total = (long long)B * H * n * n_split;
+  // block 128: one four-wave tile per query block; block 64: one four-wave
+  // tile per pair of neighbouring query blocks
+  const int n_qtiles = block == 64 ? (n + 1) / 2 : n;
+  const long long total = (long long)B * H * n_qtiles * n_split;
   if (total >= (1ll << 31)) return BA_ERR_UNSUPPORTED;
   ba::AttnParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -328,7 +331,7 @@ ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t blo
   p.lse = lse;
   p.N = N;
   p.n_blocks = n;
-  p.n_qtiles = n;
+  p.n_qtiles = n_qtiles;
   p.total = (int)total;
   p.max_keep = max_keep;
   p.scale_log2 = resolve_scale(scale, D) * 1.44269504088896340736f;
@@ -339,10 +342,10 @@ ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t blo
   p.lse_ext = lse_ext;
   p.walk_mul = walk_multiplier(n);
   if (D == 128) {
-    if (block == 64) launch_attn<128, 2, 64, true>(p, o_f32, s);
+    if (block == 64) launch_attn<128, 4, 64, true>(p, o_f32, s);
     else launch_attn<128, 4, 128, true>(p, o_f32, s);
   } else {
-    if (block == 64) launch_attn<64, 2, 64, true>(p, o_f32, s);
+    if (block == 64) launch_attn<64, 4, 64, true>(p, o_f32, s);
     else launch_attn<64, 4, 128, true>(p, o_f32, s);
   }
   return finish_launch();
@@ -390,10 +393,11 @@ int32_t ba_att_forward_split_parts(int32_t B, int32_t H, int32_t N, int32_t bloc
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
-  // resident attention workgroups per compute unit: the two-wave tile (block
-  // 64) holds 2 waves per SIMD, the four-wave tile (block 128) 3
-  const long long resident = (long long)cus * (block == 64 ? 4 : 3);
-  const long long tiles = (long long)B * H * num_blocks(N, block);
+  // resident attention workgroups per compute unit: three four-wave tiles
+  // (one query block at block 128, a pair of them at block 64)
+  const long long resident = (long long)cus * 3;
+  const int n = num_blocks(N, block);
+  const long long tiles = (long long)B * H * (block == 64 ? (n + 1) / 2 : n);
   long long parts = resident / tiles;  // the largest count that still fits one round
   parts = std::min(parts, (long long)max_keep * (block / ba::kChunk));
   parts = std::min(parts, (long long)kMaxSplit);

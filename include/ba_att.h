@@ -167,12 +167,13 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
 size_t ba_att_forward_split_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t n_split);
 
 /* Suggested n_split for ba_att_forward_split on the current device: the
- * largest P whose B*H*n*P workgroups still fit in one round of the device
- * (its compute units times the attention tile's residency per unit: 4
- * two-wave workgroups at block 64, 3 four-wave ones at block 128), at most the
- * chunks of a full list (max_keep*block/64) and 64.  1 means the unsplit
- * launch already fills the device.  Host only (one device query); returns 0
- * on invalid arguments or when the device cannot be queried. */
+ * largest P whose B*H*T*P workgroups still fit in one round of the device
+ * (its compute units times 3 resident four-wave attention tiles), with T the
+ * tiles per head (n at block 128, one per pair of query blocks, ceil(n/2),
+ * at block 64), at most the chunks of a full list (max_keep*block/64) and
+ * 64.  1 means the unsplit launch already fills the device.  Host only (one
+ * device query); returns 0 on invalid arguments or when the device cannot
+ * be queried.  (A helper of this interface, not an operation of the pages.) */
 int32_t ba_att_forward_split_parts(int32_t B, int32_t H, int32_t N, int32_t block, int32_t max_keep);
 int ba_att_forward_split(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
                          const void* q, const void* k, const void* v, const int32_t* block_idx,

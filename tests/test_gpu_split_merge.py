@@ -166,8 +166,9 @@ def test_suggested_split_fills_the_device_once(gpu_lib):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for (B, H, N, block, max_keep) in [(1, 1, 32768, 64, 256), (1, 32, 8192, 64, 64), (1, 1, 8192, 64, 64),
                                        (1, 1, 8192, 128, 32), (1, 1, 1000, 64, 2), (2, 4, 4096, 128, 16)]:
-        tiles = B * H * orc.num_blocks(N, block)
-        resident = cus * (4 if block == 64 else 3)
+        n = orc.num_blocks(N, block)
+        tiles = B * H * ((n + 1) // 2 if block == 64 else n)  # block 64: a tile per pair of query blocks
+        resident = cus * 3
         parts = gpu_lib.forward_split_parts(B, H, N, block, max_keep)
         assert 1 <= parts <= min(64, max_keep * block // 64)
         assert parts == 1 or parts * tiles <= resident        # one round
