@@ -130,6 +130,10 @@ void launch_attn(const ba::AttnParams& p, bool out_f32, hipStream_t s) {
     ba::attn_fwd_kernel<D, WAVES, BLK, SPARSE, false><<<grid, WAVES * 64, 0, s>>>(p);
 }
 
+// Workspace of the selection pass: the pooled statistics aq, ak (fp32
+// [B*H, n, 3D] each).
+size_t select_workspace_bytes(int BH, int n, int D) { return 2 * (size_t)BH * n * 3 * D * sizeof(float); }
+
 // Checks of ba_att_select's arguments other than its workspace.
 ba_status check_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, double sparsity,
                        const void* q, const void* k, const uint8_t* block_mask, const int32_t* block_idx,
@@ -185,8 +189,7 @@ int32_t ba_att_keep_count(int32_t n_blocks, double sparsity) {
 
 size_t ba_att_select_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block) {
   if (check_shape(B, H, N, D) != BA_OK || block < 1) return 0;
-  const size_t n = (size_t)num_blocks(N, block);
-  return 2 * (size_t)B * H * n * 3 * D * sizeof(float);
+  return select_workspace_bytes(B * H, num_blocks(N, block), D);
 }
 
 int ba_att_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,

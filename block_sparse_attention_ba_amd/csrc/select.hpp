@@ -43,20 +43,17 @@ __device__ __forceinline__ float xor_sum(float x, int mask) {
   return x + wave_shfl_xor(x, mask);
 }
 
+// One wave pools block gb of the 2*BH*n (tensor, head, block) triples.
 template <int D, int BLK>
-__global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ k,
-                                                         float* __restrict__ aq,
-                                                         float* __restrict__ ak, int N, int n,
-                                                         int BH, float scale) {
+__device__ __forceinline__ void pool_block(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                           float* __restrict__ aq, float* __restrict__ ak, int N, int n,
+                                           int BH, float scale, int gb) {
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int RG = 64 / CPR;      // row groups per wave
   constexpr int RPL = BLK / RG;     // rows per lane
   static_assert(BLK % RG == 0, "block must be a multiple of the row groups");
 
   const int per_tensor = BH * n;
-  const int gb = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (gb >= 2 * per_tensor) return;
   const int tensor = gb / per_tensor;
   const int rem = gb - tensor * per_tensor;
   const int bh = rem / n;
@@ -144,6 +141,17 @@ __global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restr
       reinterpret_cast<f32x4*>(out + g * D)[1] = seg[g][1];
     }
   }
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         float* __restrict__ aq,
+                                                         float* __restrict__ ak, int N, int n,
+                                                         int BH, float scale) {
+  const int gb = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gb >= 2 * BH * n) return;
+  pool_block<D, BLK>(q, k, aq, ak, N, n, BH, scale, gb);
 }
 
 // ---------------------------------------------------------------------------
@@ -290,13 +298,12 @@ __host__ __device__ constexpr int score_lds_bytes(int D, int R, int n) {
   return (R * (3 * D / 2) + R * (n + 4)) * 4;
 }
 
-template <int D, int NI, int R>
-__global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const float* __restrict__ aq,
-                                                         const float* __restrict__ ak, int n,
-                                                         int keep, uint8_t* __restrict__ mask,
-                                                         int32_t* __restrict__ idx,
-                                                         int32_t* __restrict__ cnt,
-                                                         float* __restrict__ score, int total) {
+// Rows R0 .. R0+R-1 of head bh, by a workgroup of W waves whose LDS starts at lds.
+template <int D, int NI, int R, int W>
+__device__ __forceinline__ void score_tile(const float* __restrict__ aq, const float* __restrict__ ak, int n,
+                                           int keep, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
+                                           int32_t* __restrict__ cnt, float* __restrict__ score, int bh, int R0,
+                                           float* lds) {
   constexpr int K3 = 3 * D;
   constexpr int KCH = K3 / 2;         // floats of an A row staged at a time
   constexpr int F4 = KCH / 4;         // float4 slots per staged A row
@@ -304,19 +311,12 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
   static_assert(F4 % (SWZ + 1) == 0, "swizzle must stay inside the row");
   constexpr int MST = KCH / 16;       // float4 B loads per lane per half and column tile
   constexpr int RT = R / 16;          // row tiles
-  constexpr int CTW = NI >= 4 ? NI / 4 : 1;  // column tiles per wave (4*NI tiles cover 64*NI columns)
+  constexpr int CTW = (4 * NI + W - 1) / W;  // column tiles per wave (4*NI tiles cover 64*NI columns)
   static_assert(RT * CTW <= 8, "accumulators of a wave");
-  extern __shared__ __attribute__((aligned(16))) float lds[];
   float* const Abuf = lds;                  // [R][KCH], float4 slot j of row r at j ^ (r & SWZ)
   float* const Sbuf = lds + R * KCH;        // [R][SP]
   const int SP = n + 4;
 
-  // the row tiles of one head run on one XCD and share its L2 copy of ak
-  const int logical = xcd_remap(blockIdx.x, total);
-  if (logical < 0) return;
-  const int tiles = (n + R - 1) / R;
-  const int bh = logical / tiles;
-  const int R0 = (logical - bh * tiles) * R;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (h > 0) __syncthreads();  // every wave is done with the first half
-    for (int e = threadIdx.x; e < R * F4; e += kScoreWaves * 64) {
+    for (int e = threadIdx.x; e < R * F4; e += W * 64) {
       const int row = e / F4, j = e - row * F4;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (R0 + row < n) v = *reinterpret_cast<const f32x4*>(Ah + (size_t)row * K3 + h * KCH + 4 * j);
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < CTW; ++t) {
-      const int ct = wave + kScoreWaves * t;
+      const int ct = wave + W * t;
       if (ct >= ctiles) break;
       // one column tile's B operand in flight at a time (loads hoisted from
       // later tiles would spill the accumulators of long rows)
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
   // lane holds column ct*16 + li of rows r*16 + 4*lg + {0..3}
 #pragma unroll
   for (int t = 0; t < CTW; ++t) {
-    const int ct = wave + kScoreWaves * t;
+    const int ct = wave + W * t;
     const int col = ct * 16 + li;
     if (ct < ctiles && col < n) {
 #pragma unroll
@@ -379,13 +379,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
   }
   __syncthreads();
   if (score != nullptr) {  // the score map as the selection saw it, row by row
-    for (int e = threadIdx.x; e < R * n; e += kScoreWaves * 64) {
+    for (int e = threadIdx.x; e < R * n; e += W * 64) {
       const int row = e / n, col = e - row * n;
       if (R0 + row < n) score[((size_t)bh * n + R0 + row) * n + col] = Sbuf[row * SP + col];
     }
   }
 
-  for (int r = wave; r < R; r += kScoreWaves) {
+  for (int r = wave; r < R; r += W) {
     const int I = R0 + r;
     if (I >= n) break;
     uint32_t key[NI];
@@ -397,6 +397,22 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const floa
     const size_t row = (size_t)bh * n + I;
     radix_select_row<NI>(key, n, keep, mask + row * n, idx + row * keep, cnt + row);
   }
+}
+
+template <int D, int NI, int R>
+__global__ __launch_bounds__(kScoreWaves * 64) void score_topk_kernel(const float* __restrict__ aq,
+                                                         const float* __restrict__ ak, int n,
+                                                         int keep, uint8_t* __restrict__ mask,
+                                                         int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ cnt,
+                                                         float* __restrict__ score, int total) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  // the row tiles of one head run on one XCD and share its L2 copy of ak
+  const int logical = xcd_remap(blockIdx.x, total);
+  if (logical < 0) return;
+  const int tiles = (n + R - 1) / R;
+  const int bh = logical / tiles;
+  score_tile<D, NI, R, kScoreWaves>(aq, ak, n, keep, mask, idx, cnt, score, bh, (logical - bh * tiles) * R, lds);
 }
 
 // ---------------------------------------------------------------------------

@@ -81,7 +81,7 @@ def test_select_matches_oracle(gpu_lib, case):
     # pooled statistics in the caller's workspace: [aq | ak], 3D fp32 per block
     aw = ws.view(torch.float32).cpu().numpy().astype(np.float64)
     aq = aw[: B * H * n * 3 * D].reshape(B, H, n, 3 * D)
-    ak = aw[B * H * n * 3 * D:].reshape(B, H, n, 3 * D)
+    ak = aw[B * H * n * 3 * D: 2 * B * H * n * 3 * D].reshape(B, H, n, 3 * D)
     sc = 1 / math.sqrt(D)
     assert np.allclose(aq[..., :D], sc * ref["qm"], rtol=1e-5, atol=1e-6)
     assert np.allclose(aq[..., D:2 * D], 0.5 * sc * sc * ref["qv"], rtol=1e-4, atol=1e-7)
