@@ -280,6 +280,10 @@ namespace {
 
 constexpr int kMaxSplit = 64;
 
+// The forward packs a walk entry as (key << 16) | (J << 1) | list and marks
+// an invalid entry J = 0x7FFF, so every block index must fit in 15 bits.
+static_assert(kMaxN / 64 < 0x7FFF, "block indices of the walk fit 15 bits");
+
 // Multiplier of the sparse walk order: the integer nearest n/phi (phi the
 // golden ratio) that is coprime with n, so that J -> J*g mod n permutes the
 // blocks and scatters neighbouring blocks across the walk.
