@@ -264,15 +264,36 @@ def kept_tile_flops(mask, N: int, D: int, block: int) -> float:
 
 
 def cpu_model() -> str:
-    """The host CPU's full model string (/proc/cpuinfo)."""
+    """The host CPU as /proc/cpuinfo names it: the model string with its
+    family / model / stepping numbers (a virtualised host may report only a
+    generic string), and the number of logical CPUs the host has."""
+    fields, logical = {}, 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "processor":
+                    logical += 1
+                elif key in ("model name", "cpu family", "model", "stepping", "microcode") and key not in fields:
+                    fields[key] = val.strip()
     except OSError:
-        pass
-    return "unknown host CPU"
+        return "unknown host CPU"
+    name = fields.get("model name", "unknown host CPU")
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping", "microcode") if k in fields)
+    return f"{name} ({ids}; {logical} logical CPUs on the host)" if ids else name
+
+
+def cpu_ranges(cpus) -> str:
+    """Compact form of a CPU set: {0,1,2,3,8} -> '0-3,8'."""
+    cpus, out, i = sorted(cpus), [], 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(str(cpus[i]) if i == j else f"{cpus[i]}-{cpus[j]}")
+        i = j + 1
+    return ",".join(out)
 
 
 def sample_heads(name: str, B: int, H: int, count: int) -> list:
@@ -297,7 +318,7 @@ def cpu_baseline(x, w, sp: float, heads: list) -> tuple:
     from oracle.parity import host_threads, map_heads
 
     threads = host_threads()
-    affinity = len(os.sched_getaffinity(0))
+    cpus = os.sched_getaffinity(0)
 
     def one(bh):
         a = time.perf_counter()
@@ -311,8 +332,8 @@ def cpu_baseline(x, w, sp: float, heads: list) -> tuple:
     dt = time.perf_counter() - t0
     flops = 4.0 * w.N * w.N * w.D * len(heads)
     record = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(threads, len(heads))),
-              "kind": "oracle", "host_cores_available": affinity, "thread_cap": 16,
-              "cpu_model": cpu_model(), "wall_s": round(dt, 3),
+              "kind": "oracle", "host_cores_available": len(cpus), "affinity_cpus": cpu_ranges(cpus),
+              "thread_cap": 16, "cpu_model": cpu_model(), "wall_s": round(dt, 3),
               "select_s_summed": round(sum(r[3] for r in res), 3),
               "attention_s_summed": round(sum(r[4] for r in res), 3),
               "heads": [list(h) for h in heads],

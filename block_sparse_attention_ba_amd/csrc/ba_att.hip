@@ -66,19 +66,28 @@ void launch_pool(int BH, int N, int n, int block, float scale, const uint16_t* q
     ba::pool_stats_kernel<D, 128><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
 }
 
-// Rows per score workgroup: the largest R in {64, 32, 16} whose grid of
-// B*H*ceil(n/R) workgroups still covers every compute unit and whose row
-// buffers fit the LDS (each workgroup reads its head's ak once, so fewer,
-// taller workgroups re-read it less); 16 when none covers the device.
-int score_rows(int BH, int n, int D, int NI) {
+int device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  for (int R : {64, 32}) {
-    const int ctw = NI >= 4 ? NI / 4 : 1;
-    if ((R / 16) * ctw > 8 || ba::score_lds_bytes(D, R, n) > ba::kScoreLdsBytes) continue;
-    if ((long long)BH * ((n + R - 1) / R) >= cus) return R;
+  return cus;
+}
+
+// Rows per score workgroup: the largest R in {64, 32, 16} whose grid of
+// B*H*ceil(n/R) workgroups covers every compute unit twice, else the largest
+// that covers it once, else 16; R must fit the accumulators and the LDS.
+// Each workgroup reads its head's ak once, so taller workgroups re-read it
+// less; two workgroups resident on a compute unit overlap one's row
+// selections (scalar-bound) with the other's fp32 products.
+int score_rows(int BH, int n, int D, int NI) {
+  const int cus = device_cus();
+  for (int cover : {2, 1}) {
+    for (int R : {64, 32, 16}) {
+      const int ctw = NI >= 4 ? NI / 4 : 1;
+      if ((R / 16) * ctw > 8 || ba::score_lds_bytes(D, R, n) > ba::kScoreLdsBytes) continue;
+      if ((long long)BH * ((n + R - 1) / R) >= (long long)cover * cus) return R;
+    }
   }
   return 16;
 }

@@ -200,171 +200,217 @@ __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t x) {
   return op(r[0], r[1]);
 }
 
-// Selects the `keep` largest keys of one row (ties: lower J) held as
-// key[i] for J = lane + 64*i; writes mask bytes, ascending idx and the count.
-// All control state is wave-uniform (scalar registers); per-bit counts come
-// from ballots.
-template <int NI>
-__device__ __forceinline__ void radix_select_row(const uint32_t (&key)[NI], int n, int keep,
-                                                 uint8_t* __restrict__ mask_row,
-                                                 int32_t* __restrict__ idx_row,
-                                                 int32_t* __restrict__ cnt_out) {
+// Selects the `keep` largest keys (ties: lower J) of each of P rows, row p
+// held as key[p][i] for J = lane + 64*i with key 0 in the slots J >= n;
+// writes mask bytes, ascending idx and the count of every row with
+// live[p].  All control state is wave-uniform (scalar registers) and
+// per-bit counts come from ballots.  The P searches advance together, one
+// bit per pass with no branch per row, so their dependency chains overlap.
+template <int NI, int P>
+__device__ __forceinline__ void radix_select_rows(const uint32_t (&key)[P][NI], const bool (&live)[P], int n,
+                                                  int keep, uint8_t* const (&mask_row)[P],
+                                                  int32_t* const (&idx_row)[P], int32_t* const (&cnt_out)[P]) {
   const int lane = __lane_id();
   uint64_t vmask[NI];  // lanes holding a valid J in slot i
 #pragma unroll
   for (int i = 0; i < NI; ++i) vmask[i] = __builtin_amdgcn_ballot_w64(lane + 64 * i < n);
-  // Bits above the highest bit where the largest and smallest key differ
-  // are shared by every key and need no search.
-  uint32_t kmax = 0u, kmin = ~0u;
+  // Invariant per row: the candidates are the keys whose bits above `bit`
+  // equal `prefix`; `remaining` of them are still to be taken (1 <=
+  // remaining <= cand).  Every key above the candidate range is taken.
+  // Bits above the highest bit where the row's largest and smallest key
+  // differ are shared by every key and need no search.
+  uint32_t prefix[P];
+  int remaining[P], bit[P], cand[P];
+  bool act[P];
+  bool any = false;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (lane + 64 * i < n) {
-      kmax = key[i] > kmax ? key[i] : kmax;
-      kmin = key[i] < kmin ? key[i] : kmin;
+  for (int p = 0; p < P; ++p) {
+    uint32_t kmax = 0u, kmin = ~0u;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (lane + 64 * i < n) {
+        kmax = key[p][i] > kmax ? key[p][i] : kmax;
+        kmin = key[p][i] < kmin ? key[p][i] : kmin;
+      }
     }
+    kmax = __builtin_amdgcn_readfirstlane(wave_minmax_u32<true>(kmax));
+    kmin = __builtin_amdgcn_readfirstlane(wave_minmax_u32<false>(kmin));
+    const uint32_t diff = kmax ^ kmin;
+    const int top = diff != 0u ? 31 - __builtin_clz(diff) : -1;
+    bit[p] = top;
+    prefix[p] = top < 0 ? kmax : kmax & ~((top == 31) ? ~0u : ((2u << top) - 1u));
+    remaining[p] = keep;
+    cand[p] = n;
+    act[p] = top >= 0;
+    any = any || act[p];
   }
-  kmax = __builtin_amdgcn_readfirstlane(wave_minmax_u32<true>(kmax));
-  kmin = __builtin_amdgcn_readfirstlane(wave_minmax_u32<false>(kmin));
-  const uint32_t diff = kmax ^ kmin;
-  // Invariant: the candidates are the keys whose bits above `bit` equal
-  // `prefix`; `remaining` of them are still to be taken (1 <= remaining <=
-  // cand).  Every key above the candidate range is taken.
-  uint32_t prefix = kmax;
-  int remaining = keep;
-  int bit = -1;  // bits >= bit+1 of the candidates are fixed
-  if (diff != 0u) {
-    bit = 31 - __builtin_clz(diff);
-    prefix = kmax & ~((bit == 31) ? ~0u : ((2u << bit) - 1u));
-    int cand = n;
-    for (; bit >= 0; --bit) {
-      const uint32_t hi_mask = ~0u << bit;
-      const uint32_t want = prefix | (1u << bit);
+  while (any) {
+    any = false;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int b = act[p] ? bit[p] : 0;
+      const uint32_t hi_mask = ~0u << b;
+      const uint32_t want = prefix[p] | (1u << b);
+      // keys of invalid slots are 0, which never equals `want` (bit b is set)
       int c1 = 0;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        c1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64((key[i] & hi_mask) == want) & vmask[i]);
-      if (c1 >= remaining) {
-        prefix = want;
-        cand = c1;
-      } else {
-        remaining -= c1;
-        cand -= c1;
-      }
-      if (cand == remaining) break;  // every candidate is taken
+        c1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64((key[p][i] & hi_mask) == want));
+      const bool take = c1 >= remaining[p];
+      const uint32_t np = take ? want : prefix[p];
+      const int nc = take ? c1 : cand[p] - c1;
+      const int nr = take ? remaining[p] : remaining[p] - c1;
+      const bool fin = nc == nr;  // every candidate is taken: stop at this bit
+      prefix[p] = act[p] ? np : prefix[p];
+      cand[p] = act[p] ? nc : cand[p];
+      remaining[p] = act[p] ? nr : remaining[p];
+      bit[p] = act[p] && !fin ? bit[p] - 1 : bit[p];
+      act[p] = act[p] && !fin && bit[p] >= 0;
+      any = any || act[p];
     }
   }
   // bit >= 0 (early exit): take every key whose bits >= bit are >= prefix's.
   // bit < 0: keys > prefix, plus the `remaining` lowest-J keys == prefix.
   const uint64_t lt = lanemask_lt();
-  const uint32_t cmp_mask = bit >= 0 ? (~0u << bit) : ~0u;
-  const uint32_t pre = prefix & cmp_mask;
-  int base = 0, eq_seen = 0;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int J = lane + 64 * i;
-    const bool valid = J < n;
-    const uint32_t kk = key[i] & cmp_mask;
-    uint64_t km;
-    if (bit >= 0) {
-      km = __builtin_amdgcn_ballot_w64(kk >= pre) & vmask[i];
-    } else {
-      const uint64_t eqm = __builtin_amdgcn_ballot_w64(kk == pre) & vmask[i];
-      const uint64_t gtm = __builtin_amdgcn_ballot_w64(kk > pre) & vmask[i];
-      // the lowest-J equal keys are taken until `remaining` is used up
-      uint64_t take = 0;
-      int need = remaining - eq_seen;
-      uint64_t e = eqm;
-      while (need > 0 && e != 0) {
-        const uint64_t low = e & (~e + 1);
-        take |= low;
-        e &= e - 1;
-        --need;
+  for (int p = 0; p < P; ++p) {
+    if (!live[p]) continue;
+    const uint32_t cmp_mask = bit[p] >= 0 ? (~0u << bit[p]) : ~0u;
+    const uint32_t pre = prefix[p] & cmp_mask;
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int J = lane + 64 * i;
+      const bool valid = J < n;
+      const uint32_t kk = key[p][i] & cmp_mask;
+      uint64_t km;
+      if (bit[p] >= 0) {
+        km = __builtin_amdgcn_ballot_w64(kk >= pre) & vmask[i];
+      } else {
+        const uint64_t eqm = __builtin_amdgcn_ballot_w64(kk == pre) & vmask[i];
+        const uint64_t gtm = __builtin_amdgcn_ballot_w64(kk > pre) & vmask[i];
+        // the lowest-J equal keys are taken until `remaining` is used up
+        uint64_t take = 0;
+        int need = remaining[p] - eq_seen;
+        uint64_t e = eqm;
+        while (need > 0 && e != 0) {
+          const uint64_t low = e & (~e + 1);
+          take |= low;
+          e &= e - 1;
+          --need;
+        }
+        eq_seen += __builtin_popcountll(eqm);
+        km = gtm | take;
       }
-      eq_seen += __builtin_popcountll(eqm);
-      km = gtm | take;
+      const bool kept = (km >> lane) & 1;
+      const int pos = base + __builtin_popcountll(km & lt);
+      if (kept && pos < keep) idx_row[p][pos] = J;  // exactly `keep` are kept; the bound is defensive
+      base += __builtin_popcountll(km);
+      if (valid) mask_row[p][J] = kept ? 1 : 0;
     }
-    const bool kept = (km >> lane) & 1;
-    const int pos = base + __builtin_popcountll(km & lt);
-    if (kept && pos < keep) idx_row[pos] = J;  // exactly `keep` are kept; the bound is defensive
-    base += __builtin_popcountll(km);
-    if (valid) mask_row[J] = kept ? 1 : 0;
+    if (lane == 0) *cnt_out[p] = base;
   }
-  if (lane == 0) *cnt_out = base;
 }
 
-// LDS bytes of one score workgroup: the A half-tile [R][3D/2] and the score
-// rows [R][n + 4] (fp32).
+// LDS bytes of one score workgroup: the A tile [R][3D] (fp32) while the
+// products run, then, in the same memory, the score rows [R][n + 4].
 __host__ __device__ constexpr int score_lds_bytes(int D, int R, int n) {
-  return (R * (3 * D / 2) + R * (n + 4)) * 4;
+  return (3 * D > n + 4 ? R * 3 * D : R * (n + 4)) * 4;
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3): loads past
+// the end return zero, which stands for the rows and columns beyond n.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t score_rsrc(const float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ f32x4 load_f32x4(__amdgpu_buffer_rsrc_t rs, int byte_offset) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_offset, 0, 0));
 }
 
 // Rows R0 .. R0+R-1 of head bh, by a workgroup of W waves whose LDS starts at lds.
+//
+// The whole A tile (aq rows) is staged in LDS with every load in flight
+// before the first write; the B operand (ak) streams through registers, PF
+// float4 loads ahead of the MFMAs that use them.  Buffer loads return zero
+// past row/column n, so no load is predicated and the compiler can wait for
+// each one by count instead of for all of them.
 template <int D, int NI, int R, int W>
 __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const float* __restrict__ ak, int n,
                                            int keep, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
                                            int32_t* __restrict__ cnt, float* __restrict__ score, int bh, int R0,
                                            float* lds) {
   constexpr int K3 = 3 * D;
-  constexpr int KCH = K3 / 2;         // floats of an A row staged at a time
-  constexpr int F4 = KCH / 4;         // float4 slots per staged A row
-  constexpr int SWZ = (F4 % 16 == 0) ? 15 : 7;  // slot swizzle within aligned groups of F4
+  constexpr int F4 = K3 / 4;          // float4 slots per A row
+  constexpr int SWZ = 15;             // slot swizzle within aligned groups of 16 slots
   static_assert(F4 % (SWZ + 1) == 0, "swizzle must stay inside the row");
-  constexpr int MST = KCH / 16;       // float4 B loads per lane per half and column tile
+  constexpr int KS = K3 / 16;         // K steps: one float4 of B per lane and step
   constexpr int RT = R / 16;          // row tiles
   constexpr int CTW = (4 * NI + W - 1) / W;  // column tiles per wave (4*NI tiles cover 64*NI columns)
+  constexpr int STEPS = CTW * KS;
+  constexpr int PF = STEPS < 8 ? STEPS : 8;  // B loads in flight per lane
+  constexpr int T = W * 64;
+  constexpr int AL = (R * F4 + T - 1) / T;  // A float4 loads per thread
   static_assert(RT * CTW <= 8, "accumulators of a wave");
-  float* const Abuf = lds;                  // [R][KCH], float4 slot j of row r at j ^ (r & SWZ)
-  float* const Sbuf = lds + R * KCH;        // [R][SP]
+  float* const Abuf = lds;  // [R][K3], float4 slot j of row r at j ^ (r & SWZ)
+  float* const Sbuf = lds;  // [R][SP], once every wave is done with Abuf
   const int SP = n + 4;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int ctiles = (n + 15) / 16;
-  const float* const Ah = aq + ((size_t)bh * n + R0) * K3;
-  const float* const Bh = ak + (size_t)bh * n * K3;
+  const int rows_here = min(R, n - R0);
+  const auto a_rs = score_rsrc(aq + ((size_t)bh * n + R0) * K3, rows_here * K3 * 4);
+  const auto b_rs = score_rsrc(ak + (size_t)bh * n * K3, n * K3 * 4);
+  // step s = (column tile t of this wave, K step m); lane (li, lg) takes
+  // k = 16m + 4lg + e for MFMA e of the step in both operands
+  auto b_offset = [&](int s) {
+    const int t = s / KS, m = s - t * KS;
+    return (((wave + W * t) * 16 + li) * K3 + 16 * m + 4 * lg) * 4;
+  };
+
+  f32x4 av[AL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) av[i] = load_f32x4(a_rs, (threadIdx.x + i * T) * 16);
+  f32x4 b[PF];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) b[s] = load_f32x4(b_rs, b_offset(s));
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int e = threadIdx.x + i * T;
+    if ((R * F4) % T == 0 || e < R * F4) {
+      const int row = e / F4, j = e - row * F4;
+      *reinterpret_cast<f32x4*>(Abuf + row * K3 + 4 * (j ^ (row & SWZ))) = av[i];
+    }
+  }
+  __syncthreads();
 
   f32x4 acc[CTW][RT];
 #pragma unroll
   for (int t = 0; t < CTW; ++t)
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h > 0) __syncthreads();  // every wave is done with the first half
-    for (int e = threadIdx.x; e < R * F4; e += W * 64) {
-      const int row = e / F4, j = e - row * F4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (R0 + row < n) v = *reinterpret_cast<const f32x4*>(Ah + (size_t)row * K3 + h * KCH + 4 * j);
-      *reinterpret_cast<f32x4*>(Abuf + row * KCH + 4 * (j ^ (row & SWZ))) = v;
-    }
-    __syncthreads();
+  for (int s = 0; s < STEPS; ++s) {
+    const int t = s / KS, m = s - t * KS;
+    if (wave + W * t < ctiles) {
+      f32x4 a[RT];
 #pragma unroll
-    for (int t = 0; t < CTW; ++t) {
-      const int ct = wave + W * t;
-      if (ct >= ctiles) break;
-      // one column tile's B operand in flight at a time (loads hoisted from
-      // later tiles would spill the accumulators of long rows)
-      __builtin_amdgcn_sched_barrier(0);
-      const int col = ct * 16 + li;
-      const float* Bp = Bh + (size_t)col * K3 + h * KCH + 4 * lg;
-      f32x4 b[MST];
-#pragma unroll
-      for (int m = 0; m < MST; ++m)
-        b[m] = col < n ? *reinterpret_cast<const f32x4*>(Bp + 16 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < MST; ++m) {
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const int row = r * 16 + li;
-          const f32x4 a = *reinterpret_cast<const f32x4*>(Abuf + row * KCH + 4 * ((4 * m + lg) ^ (row & SWZ)));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[m][e], acc[t][r], 0, 0, 0);
-        }
+      for (int r = 0; r < RT; ++r) {
+        const int row = r * 16 + li;
+        a[r] = *reinterpret_cast<const f32x4*>(Abuf + row * K3 + 4 * ((4 * m + lg) ^ (row & SWZ)));
       }
+      // row tiles innermost: consecutive MFMAs of a wave use different accumulators
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r][e], b[s % PF][e], acc[t][r], 0, 0, 0);
     }
+    if (s + PF < STEPS) b[s % PF] = load_f32x4(b_rs, b_offset(s + PF));
   }
+  __syncthreads();  // the score rows overwrite the A tile
   // lane holds column ct*16 + li of rows r*16 + 4*lg + {0..3}
 #pragma unroll
   for (int t = 0; t < CTW; ++t) {
@@ -385,17 +431,33 @@ __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const f
     }
   }
 
-  for (int r = wave; r < R; r += W) {
-    const int I = R0 + r;
-    if (I >= n) break;
-    uint32_t key[NI];
+  // wave w selects rows w, w + W, ...: RP of them at a time
+  constexpr int RW = (R + W - 1) / W;
+  constexpr int RP = NI <= 8 ? (RW < 4 ? RW : 4) : 1;
+  for (int r0 = wave; r0 < R; r0 += W * RP) {
+    if (R0 + r0 >= n) break;
+    uint32_t key[RP][NI];
+    bool live[RP];
+    uint8_t* mrow[RP];
+    int32_t* irow[RP];
+    int32_t* crow[RP];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int J = lane + 64 * i;
-      key[i] = (J < n) ? float_order_key(Sbuf[r * SP + J]) : 0u;
+    for (int p = 0; p < RP; ++p) {
+      const int r = min(r0 + W * p, R - 1);
+      const int I = R0 + r;
+      live[p] = r0 + W * p < R && I < n;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int J = lane + 64 * i;
+        const uint32_t k = float_order_key(Sbuf[r * SP + min(J, n - 1)]);
+        key[p][i] = J < n ? k : 0u;
+      }
+      const size_t row = (size_t)bh * n + min(I, n - 1);
+      mrow[p] = mask + row * n;
+      irow[p] = idx + row * keep;
+      crow[p] = cnt + row;
     }
-    const size_t row = (size_t)bh * n + I;
-    radix_select_row<NI>(key, n, keep, mask + row * n, idx + row * keep, cnt + row);
+    radix_select_rows<NI, RP>(key, live, n, keep, mrow, irow, crow);
   }
 }
 

@@ -66,7 +66,7 @@ def test_cpu_baseline_and_parity_report_on_the_tiny_workload():
     w = x["workload"]
     rec, per_head = bench.cpu_baseline(x, w, 0.5, [(0, 0)])
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["heads"] == [[0, 0]]
-    assert rec["host_cores_available"] >= 1 and rec["cpu_model"]
+    assert rec["host_cores_available"] >= 1 and rec["cpu_model"] and rec["affinity_cpus"]
     mask, O, L = per_head[(0, 0)]
     ref = orc.select_oracle(x["q"], x["k"], w.block, 0.5)
     assert np.array_equal(mask, ref["mask"][0, 0])

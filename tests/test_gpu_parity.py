@@ -55,6 +55,10 @@ SELECT_CASES = [
     (1, 1, 16384, 64, 64, 0.5, "normal"),       # 256 blocks per row
     (1, 1, 20000, 128, 64, 0.5, "clustered"),   # 313 blocks: 5 elements per lane
     (1, 2, 1024, 128, 64, 0.95, "clustered"),   # keep = 1 of 16: the row maximum alone
+    # many heads: score grids that cover the device twice (two workgroups per CU)
+    (1, 256, 2000, 64, 64, 0.5, "clustered"),   # n = 32: 14 of 16 waves without a column tile
+    (1, 40, 12790, 128, 64, 0.5, "normal"),     # n = 200, ragged last block and row tile
+    (1, 27, 19193, 64, 64, 0.75, "clustered"),  # n = 300: column tiles past n
 ]
 
 
