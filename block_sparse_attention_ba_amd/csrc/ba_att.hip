@@ -74,16 +74,21 @@ int device_cus() {
   return cus;
 }
 
-// Rows per score workgroup: the largest R in {64, 32, 16} whose grid of
+// Rows per score workgroup: the largest R with a kernel for this row length
+// (64 up to n = 256, 32 up to n = 1024, else 16) whose grid of
 // B*H*ceil(n/R) workgroups covers every compute unit twice, else the largest
 // that covers it once, else 16; R must fit the accumulators and the LDS.
 // Each workgroup reads its head's ak once, so taller workgroups re-read it
-// less; two workgroups resident on a compute unit overlap one's row
-// selections (scalar-bound) with the other's fp32 products.
+// less.  Up to n = 256 the kernels keep to 64 VGPRs, so two workgroups share
+// a compute unit and one's row selections (scalar-bound) overlap the other's
+// fp32 products; longer rows take more registers and only the single cover
+// applies.
 int score_rows(int BH, int n, int D, int NI) {
   const int cus = device_cus();
   for (int cover : {2, 1}) {
+    if (cover == 2 && NI > 4) continue;
     for (int R : {64, 32, 16}) {
+      if ((R == 64 && NI > 4) || (R == 32 && NI > 16)) continue;
       const int ctw = NI >= 4 ? NI / 4 : 1;
       if ((R / 16) * ctw > 8 || ba::score_lds_bytes(D, R, n) > ba::kScoreLdsBytes) continue;
       if ((long long)BH * ((n + R - 1) / R) >= (long long)cover * cus) return R;
