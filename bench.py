@@ -46,11 +46,21 @@ KERNEL_SOURCES = {
 }
 
 
+def source_code_text(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed, so that a
+    comment edit leaves the hash of the code unchanged (string literals in
+    the kernels hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(source_code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -156,24 +156,25 @@ __global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restr
 
 // ---------------------------------------------------------------------------
 // Compact score and norm sort.  One workgroup of 16 waves per (b*h, R
-// consecutive query-block rows), R in {16, 32, 64} chosen by the host so that
-// the grid still covers the device: every workgroup reads its head's ak once,
-// so larger R means fewer re-reads of ak.
+// consecutive query-block rows), R in {16, 32, 64} chosen by the host: every
+// workgroup reads its head's ak once, so larger R means fewer re-reads of ak,
+// and two workgroups resident on a compute unit overlap one's selections with
+// the other's products.
 //
 // S = aq . ak^T is a small fp32 GEMM (K = 3D) done with
 // v_mfma_f32_16x16x4_f32 on 16x16 output tiles.  Wave w owns the column
 // tiles w, w + 16, ... and every row tile of them, so the B operand (ak,
-// loaded from L2 as float4 per lane) is read once per workgroup and reused
-// for the R/16 row tiles; the A operand (aq) is staged in LDS in two halves
-// of K, its float4 slots XOR-swizzled by the row so that the 16 rows of a
-// tile hit distinct banks.  Lane group g takes k = 16m + 4g + e for MFMA
+// streamed from L2 as float4 buffer loads per lane) is read once per
+// workgroup and reused for the R/16 row tiles; the A operand (aq) is staged
+// whole in LDS, its float4 slots XOR-swizzled by the row so that the 16 rows
+// of a tile hit distinct banks.  Lane group g takes k = 16m + 4g + e for MFMA
 // step (m, e) in both operands (a permutation of k, so the product is
 // unchanged); every tile accumulates its K steps in the same order whatever
-// R is, so S does not depend on R.  The accumulators stay in registers over
-// both halves and then go to an LDS row buffer [R][n + 4]; one wave per row
-// then selects the `keep` largest scores (ties to lower J) by an MSB-first
-// radix select over order-preserving uint32 keys and writes mask, ascending
-// idx and cnt.
+// R is, so S does not depend on R.  The accumulators then go to an LDS row
+// buffer [R][n + 4] that reuses the A tile's memory; each wave selects the
+// `keep` largest scores (ties to lower J) of its rows, several rows per
+// search, by an MSB-first radix select over order-preserving uint32 keys and
+// writes mask, ascending idx and cnt.
 // ---------------------------------------------------------------------------
 constexpr int kMaxScoreBlocks = 2048;  // longest row
 constexpr int kScoreWaves = 16;

@@ -91,3 +91,14 @@ def test_cpu_baseline_and_parity_report_on_the_tiny_workload():
     rep2 = bench.parity_report(x, w, 0.5, gmask2, {(0, 0): O}, {(0, 0): L}, per_head)
     assert not rep2["pass"] and rep2["bad_rows"] == 1
     assert rep2["o_rows_skipped_near_tie"] == w.block  # that row's tokens are not compared
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    """The traffic counters stay valid across comment edits of a kernel's
+    sources, and not across code edits."""
+    import bench
+    code = "int f(int x) {\n  return x + 1;  // one\n}\n/* block\n comment */\n"
+    assert bench.source_code_text(code) == bench.source_code_text("int f(int x) { return x + 1; }")
+    assert bench.source_code_text(code) != bench.source_code_text("int f(int x) { return x + 2; }")
+    for kind in bench.KERNEL_SOURCES:
+        assert len(bench.kernel_source_hash(kind)) == 16
