@@ -59,6 +59,8 @@ SELECT_CASES = [
     (1, 256, 2000, 64, 64, 0.5, "clustered"),   # n = 32: 14 of 16 waves without a column tile
     (1, 40, 12790, 128, 64, 0.5, "normal"),     # n = 200, ragged last block and row tile
     (1, 27, 19193, 64, 64, 0.75, "clustered"),  # n = 300: column tiles past n
+    (1, 128, 16384, 64, 64, 0.5, "normal"),     # 64-row score tiles: four rows per radix search
+    (1, 128, 16384, 128, 64, 0.5, "normal"),
 ]
 
 
