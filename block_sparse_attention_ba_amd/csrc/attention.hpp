@@ -395,79 +395,79 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     bf16x8 pf[4];  // P^T operand of each 16-key step
     if (mine) {
-    // S^T (64 keys x 32 queries) = K Q^T, K operands read one k-step ahead
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    bf16x8 kcur[2] = {read_k(0, 0), read_k(1, 0)};
+      // S^T (64 keys x 32 queries) = K Q^T, K operands read one k-step ahead
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      bf16x8 kcur[2] = {read_k(0, 0), read_k(1, 0)};
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      bf16x8 knext[2];
-      if (ks + 1 < KSTEPS) {
-        knext[0] = read_k(0, ks + 1);
-        knext[1] = read_k(1, ks + 1);
-      }
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qf[ks], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[1], qf[ks], sacc[1], 0, 0, 0);
-      if (ks + 1 < KSTEPS) {
-        kcur[0] = knext[0];
-        kcur[1] = knext[1];
-      }
-    }
-    // keys past the end of the sequence (or of a skipped entry)
-    if (valid < kChunk) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= valid) sacc[kt][r] = -__builtin_inff();
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        bf16x8 knext[2];
+        if (ks + 1 < KSTEPS) {
+          knext[0] = read_k(0, ks + 1);
+          knext[1] = read_k(1, ks + 1);
         }
-    }
-    // two chains of three-input maxima (v_max3_f32): 17 instructions for 32 values
-    float ma = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
-    float mb = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) {
-      ma = fmaxf(fmaxf(ma, sacc[0][r]), sacc[0][r + 1]);
-      mb = fmaxf(fmaxf(mb, sacc[1][r]), sacc[1][r + 1]);
-    }
-    float mloc = fmaxf(fmaxf(ma, sacc[0][15]), fmaxf(mb, sacc[1][15]));
-    mloc = pair_max(mloc) * sl2;
-    if (__any(mloc > m_run)) {  // exact running max: a row's largest probability is 1
-      const float m_new = fmaxf(m_run, mloc);
-      if (m_new != -__builtin_inff()) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
-        m_run = m_new;
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qf[ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[1], qf[ks], sacc[1], 0, 0, 0);
+        if (ks + 1 < KSTEPS) {
+          kcur[0] = knext[0];
+          kcur[1] = knext[1];
+        }
       }
-    }
-    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+      // keys past the end of the sequence (or of a skipped entry)
+      if (valid < kChunk) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= valid) sacc[kt][r] = -__builtin_inff();
+          }
+      }
+      // two chains of three-input maxima (v_max3_f32): 17 instructions for 32 values
+      float ma = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+      float mb = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) {
+        ma = fmaxf(fmaxf(ma, sacc[0][r]), sacc[0][r + 1]);
+        mb = fmaxf(fmaxf(mb, sacc[1][r]), sacc[1][r + 1]);
+      }
+      float mloc = fmaxf(fmaxf(ma, sacc[0][15]), fmaxf(mb, sacc[1][15]));
+      mloc = pair_max(mloc) * sl2;
+      if (__any(mloc > m_run)) {  // exact running max: a row's largest probability is 1
+        const float m_new = fmaxf(m_run, mloc);
+        if (m_new != -__builtin_inff()) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+          m_run = m_new;
+        }
+      }
+      const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
-    float psum = 0.f;
+      float psum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 w;
+        for (int s = 0; s < 2; ++s) {
+          u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s + 2 * e], sl2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s + 2 * e + 1], sl2, -m_use));
-          psum += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s + 2 * e], sl2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s + 2 * e + 1], sl2, -m_use));
+            psum += p0 + p1;
+            w[e] = pack_bf16x2(p0, p1);
+          }
+          pf[2 * kt + s] = __builtin_bit_cast(bf16x8, w);
         }
-        pf[2 * kt + s] = __builtin_bit_cast(bf16x8, w);
       }
-    }
-    l_run += psum;
-    // Four-wave tiles: keep the softmax ahead of the wait for V(c) so that it
-    // covers the copy (without the fence the compiler sinks it past the
-    // barrier, next to its use in O^T += V^T P^T).  Two-wave tiles are faster
-    // with the sunk form, where the exponentials fill the gaps between the
-    // PV MFMAs and the copy of K(c+1) starts earlier.
-    if constexpr (WAVES == 4)
-      __asm__ volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l_run));
+      l_run += psum;
+      // Four-wave tiles: keep the softmax ahead of the wait for V(c) so that it
+      // covers the copy (without the fence the compiler sinks it past the
+      // barrier, next to its use in O^T += V^T P^T).  Two-wave tiles are faster
+      // with the sunk form, where the exponentials fill the gaps between the
+      // PV MFMAs and the copy of K(c+1) starts earlier.
+      if constexpr (WAVES == 4)
+        __asm__ volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l_run));
     }
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(c) landed
