@@ -9,6 +9,7 @@ O within 1e-2 and LSE within 1e-3 with fp32 output; the split result also
 within 2^-8 max|v| of the unsplit one."""
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -48,7 +49,8 @@ def make_inputs(B, H, N, D, seed):
     return wl.f32_to_bf16_bits(q), wl.f32_to_bf16_bits(k), wl.f32_to_bf16_bits(v)
 
 
-@pytest.mark.parametrize("seed", range(16))
+# 16 seeds by default; BA_RANDOM_SHAPES=<count> widens the sweep
+@pytest.mark.parametrize("seed", range(int(os.environ.get("BA_RANDOM_SHAPES", "16"))))
 def test_random_shape_all_paths(gpu_lib, seed):
     import torch
     B, H, N, D, block, sp, ns = random_case(seed)
