@@ -300,29 +300,34 @@ def test_forward_list_contract_edge_cases(gpu_lib, block):
 
 
 def check_rows_against_lists(q, k, v, idx, cnt, block, max_keep, results, blocks=None):
-    """Every row of the query blocks `blocks` (default: all) of every result
-    against textbook attention over exactly the multiset of keys its clamped
-    list names (entries outside [0, n) skipped).  fp32 output to O_TOL; bf16
-    output adds its own rounding, half an ulp of the largest |O|."""
+    """Every row of the query blocks `blocks` (default: all) of every batch,
+    head and result against textbook attention over exactly the multiset of
+    keys its clamped list names (entries outside [0, n) skipped).  fp32
+    output to O_TOL; bf16 output adds its own rounding, half an ulp of the
+    largest |O|."""
     B, H, N, D = q.shape
     n = orc.num_blocks(N, block)
-    qq, kk, vv = (orc.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
     scale = 1.0 / math.sqrt(D)
-    for path, (o, lse) in results.items():
-        bf16 = str(o.dtype) == "torch.bfloat16"
-        o, lse = o[0, 0].float().cpu().numpy(), lse[0, 0].cpu().numpy()
-        for I in (range(n) if blocks is None else blocks):
-            rows = np.arange(I * block, min((I + 1) * block, N))
-            c = min(max(int(cnt[0, 0, I]), 0), max_keep)
-            keys = [t for J in idx[0, 0, I, :c] if 0 <= J < n for t in range(J * block, min((J + 1) * block, N))]
-            if not keys:
-                assert np.all(o[rows] == 0) and np.all(np.isneginf(lse[rows])), (path, I)
-                continue
-            keys = np.asarray(keys)
-            Oe, Le = orc.dense_attention(qq[rows], kk[keys], vv[keys], scale)
-            tol = O_TOL + (float(np.abs(Oe).max()) * 2.0 ** -9 if bf16 else 0.0)
-            assert max_abs(o[rows], Oe) <= tol, (path, I, max_abs(o[rows], Oe))
-            assert max_abs(lse[rows], Le) <= LSE_TOL, (path, I, max_abs(lse[rows], Le))
+    outs = {path: (o.float().cpu().numpy(), lse.cpu().numpy(), str(o.dtype) == "torch.bfloat16")
+            for path, (o, lse) in results.items()}
+    for b in range(B):
+        for h in range(H):
+            qq, kk, vv = (orc.bf16_bits_to_f64(x[b, h]) for x in (q, k, v))
+            for path, (o_all, lse_all, bf16) in outs.items():
+                o, lse = o_all[b, h], lse_all[b, h]
+                for I in (range(n) if blocks is None else blocks):
+                    rows = np.arange(I * block, min((I + 1) * block, N))
+                    c = min(max(int(cnt[b, h, I]), 0), max_keep)
+                    keys = [t for J in idx[b, h, I, :c] if 0 <= J < n
+                            for t in range(J * block, min((J + 1) * block, N))]
+                    if not keys:
+                        assert np.all(o[rows] == 0) and np.all(np.isneginf(lse[rows])), (path, b, h, I)
+                        continue
+                    keys = np.asarray(keys)
+                    Oe, Le = orc.dense_attention(qq[rows], kk[keys], vv[keys], scale)
+                    tol = O_TOL + (float(np.abs(Oe).max()) * 2.0 ** -9 if bf16 else 0.0)
+                    assert max_abs(o[rows], Oe) <= tol, (path, b, h, I, max_abs(o[rows], Oe))
+                    assert max_abs(lse[rows], Le) <= LSE_TOL, (path, b, h, I, max_abs(lse[rows], Le))
 
 
 def _forward_case(gpu_lib, q, k, v, idx, cnt, block, paths):
