@@ -70,8 +70,9 @@ struct AttnParams {
   const float* lse_ext;
   // sparse walk order: a row's kept blocks are visited in increasing
   // (J * walk_mul) mod n_blocks, one order shared by every row of every head
-  // (0: the list's own order)
+  // (0: the list's own order); walk_inv is its inverse mod n_blocks
   int walk_mul;
+  int walk_inv;
 };
 
 // Longest block list a workgroup reorders (longer lists are walked as given).
@@ -216,11 +217,14 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
     // walks the union of its two lists in that order, each entry tagged with
     // the blocks that keep it, so a block both keep is copied to LDS once.
     //
-    // The walk is built by a stable rank sort of packed words
-    // (key << 16 | J << 1 | list), so an entry of the second list follows
-    // the equal entry of the first, and merging each such pair into one
-    // entry keeps repeated entries' multiplicity; entries outside [0, n)
-    // sort last.  It is stored in this tile's own output rows, which hold
+    // The walk is built by a rank sort of packed words
+    // (key << 16 | list << 15 | position).  The key fixes the block (J is
+    // key * walk_mul^-1 mod n), so the words order the entries by key, then
+    // the first list before the second, then list position; the position
+    // makes every word unique, so an entry's rank is the number of smaller
+    // words.  Merging each entry of the second list into an entry of the
+    // first for the same block just before it keeps repeated entries'
+    // multiplicity; entries outside [0, n) take key 0xFFFF and sort last.  It is stored in this tile's own output rows, which hold
     // nothing else until the epilogue: every wave passes two barriers after
     // its last walk read before any output is written.  Full lists keep
     // ascending order (then the walk equals the dense one); a walk longer
@@ -240,51 +244,72 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
       int32_t* const out = reinterpret_cast<int32_t*>(
           reinterpret_cast<uint8_t*>(p.o) +
           (part * p.o_part_stride + ((size_t)bh * N + (size_t)qt * ROWS) * D) * out_elem);
-      for (int e = threadIdx.x; e < tot; e += T) {
-        const bool inB = e >= cA;
-        const int J = inB ? listB[e - cA] : listA[e];
-        const uint32_t own = inB ? 1u : 0u;
-        const uint32_t key = full ? (uint32_t)J : (uint32_t)((J * p.walk_mul) % n);
-        keys[e] = (J >= 0 && J < n) ? (key << 16) | ((uint32_t)J << 1) | own : (0xFFFFFFFEu | own);
+      // the packed words, padded to whole 16-byte groups with all-ones words,
+      // which are above every word and add to no rank
+      const int tot4 = (tot + 3) >> 2;
+      for (int e = threadIdx.x; e < 4 * tot4; e += T) {
+        uint32_t w = 0xFFFFFFFFu;
+        if (e < tot) {
+          const bool inB = e >= cA;
+          const int J = inB ? listB[e - cA] : listA[e];
+          const uint32_t own = inB ? 1u : 0u;
+          const uint32_t key = full ? (uint32_t)J : (uint32_t)J * (uint32_t)p.walk_mul % (uint32_t)n;
+          w = ((J >= 0 && J < n) ? key << 16 : 0xFFFF0000u) | (own << 15) | (uint32_t)e;
+        }
+        keys[e] = w;
       }
       __syncthreads();
+      // rank = number of smaller words; every lane reads the same 16 bytes
+      // (a broadcast), several in flight
+      const u32x4* const keys4 = reinterpret_cast<const u32x4*>(keys);
       for (int e = threadIdx.x; e < tot; e += T) {
         const uint32_t v = keys[e];
         int rank = 0;
-        for (int j = 0; j < tot; ++j) {
-          const uint32_t w = keys[j];
-          rank += (w < v) || (w == v && j < e);
+#pragma unroll 4
+        for (int j4 = 0; j4 < tot4; ++j4) {
+          const u32x4 w = keys4[j4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rank += w[i] < v;
         }
         sorted[rank] = v;
       }
       __syncthreads();
-      // an entry of the second list merges into an equal entry of the first
-      // just before it; every other sorted entry starts a walk entry
+      // an entry of the second list merges into an entry of the first for
+      // the same key just before it; every other sorted entry starts a walk
+      // entry
       auto starts = [&](int r) -> bool {
         if (r == 0) return true;
         const uint32_t v = sorted[r], u = sorted[r - 1];
-        return !((v >> 1) == (u >> 1) && (v & 1u) && !(u & 1u));
+        return !((v >> 16) == (u >> 16) && ((v >> 15) & 1u) && !((u >> 15) & 1u));
       };
       const int seg = (tot + T - 1) / T;
       const int s0 = min(tot, (int)threadIdx.x * seg), s1 = min(tot, s0 + seg);
       int mine_starts = 0;
       for (int r = s0; r < s1; ++r) mine_starts += starts(r);
-      scan[threadIdx.x] = mine_starts;
-      __syncthreads();
-      for (int off = 1; off < T; off <<= 1) {  // inclusive scan of the per-thread counts
-        const int add = (int)threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
-        __syncthreads();
-        scan[threadIdx.x] += add;
-        __syncthreads();
+      // exclusive scan of the per-thread counts: within each wave by lane
+      // shuffles, then over the waves' totals
+      int incl = mine_starts;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
       }
-      int pos = scan[threadIdx.x] - mine_starts;
-      const int walk_len = scan[T - 1];
+      if (lane == 63) scan[wave] = incl;
+      __syncthreads();
+      int pos = incl - mine_starts, walk_len = 0;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const int t = scan[w];
+        if (w < wave) pos += t;
+        walk_len += t;
+      }
       for (int r = s0; r < s1; ++r) {
         if (!starts(r)) continue;
-        const uint32_t v = sorted[r];
-        uint32_t own_bits = 1u << (v & 1u);
+        const uint32_t v = sorted[r], key = v >> 16;
+        uint32_t own_bits = 1u << ((v >> 15) & 1u);
         if (r + 1 < tot && !starts(r + 1)) own_bits |= 2u;
-        out[pos++] = (int32_t)((own_bits << 16) | ((v >> 1) & 0x7FFFu));
+        const uint32_t J = key == 0xFFFFu ? 0x7FFFu : full ? key : key * (uint32_t)p.walk_inv % (uint32_t)n;
+        out[pos++] = (int32_t)((own_bits << 16) | J);
       }
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the walk is in L2
       __syncthreads();

@@ -294,8 +294,10 @@ namespace {
 
 constexpr int kMaxSplit = 64;
 
-// The forward packs a walk entry as (key << 16) | (J << 1) | list and marks
-// an invalid entry J = 0x7FFF, so every block index must fit in 15 bits.
+// The forward sorts packed words (key << 16) | (list << 15) | position, with
+// key 0xFFFF for an invalid entry, and stores a walk entry's block index in
+// 15 bits with 0x7FFF for an invalid one, so every block index must fit in
+// 15 bits below 0x7FFF.
 static_assert(kMaxN / 64 < 0x7FFF, "block indices of the walk fit 15 bits");
 
 // Multiplier of the sparse walk order: the integer nearest n/phi (phi the
@@ -310,6 +312,18 @@ int walk_multiplier(int n) {
     if (g0 + d < n && gcd(g0 + d, n) == 1) return g0 + d;
   }
   return 1;
+}
+
+// Inverse of the walk multiplier mod n (extended Euclid; the multiplier is
+// coprime with n), so that the block of a walk key is key * inverse mod n.
+int walk_inverse(int m, int n) {
+  if (n <= 1) return 0;
+  long long r0 = n, r1 = m % n, t0 = 0, t1 = 1;
+  while (r1 != 0) {
+    const long long q = r0 / r1, r2 = r0 - q * r1, t2 = t0 - q * t1;
+    r0 = r1; r1 = r2; t0 = t1; t1 = t2;
+  }
+  return (int)(((t0 % n) + n) % n);
 }
 
 // Checks of the arguments every forward variant shares.
@@ -362,6 +376,7 @@ ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t blo
   p.o_ext = o_ext;
   p.lse_ext = lse_ext;
   p.walk_mul = walk_multiplier(n);
+  p.walk_inv = walk_inverse(p.walk_mul, n);
   if (D == 128) {
     if (block == 64) launch_attn<128, 4, 64, true>(p, o_f32, s);
     else launch_attn<128, 4, 128, true>(p, o_f32, s);
