@@ -436,22 +436,27 @@ def power_sample(run, stream, seconds: float) -> dict:
     return {"mean_ms_per_call": round(ms, 5), "samples": samples}
 
 
-def mfma_loop_power(dev, stream, seconds: float) -> dict:
-    """Socket power and clocks while the bf16 MFMA peak loop (libba_peaks.so:
-    2 waves per SIMD, 4 independent MFMA chains, no memory traffic) runs back
-    to back: what the matrix pipes alone draw at full rate."""
+def mfma_loop_power(dev, stream, seconds: float, random_operands: bool = False) -> dict:
+    """Socket power and clocks while a bf16 MFMA peak loop (libba_peaks.so:
+    2 waves per SIMD, independent MFMA chains, no memory traffic) runs back to
+    back: what the matrix pipes alone draw at full rate, on constant operands
+    or on random ones (eight operand pairs cycled per wave)."""
     import torch
     from block_sparse_attention_ba_amd import _lib
     pk = _lib.load_peaks()
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(n_cu * 2 * 256, dtype=torch.float32, device=dev)
+    iters, per_iter = (5000, 8) if random_operands else (20000, 4)
 
     def run():
-        if pk.ba_peak_mfma_bf16(sink.data_ptr(), n_cu * 2, 20000, 2.0 ** -10, stream.cuda_stream) != 0:
+        rc = (pk.ba_peak_mfma_bf16_random(sink.data_ptr(), n_cu * 2, iters, 12345, stream.cuda_stream)
+              if random_operands else
+              pk.ba_peak_mfma_bf16(sink.data_ptr(), n_cu * 2, iters, 2.0 ** -10, stream.cuda_stream))
+        if rc != 0:
             raise RuntimeError("peak microbenchmark launch failed")
 
     res = power_sample(run, stream, seconds)
-    res["tflops"] = round(n_cu * 2 * 4 * 20000 * 4 * 32768 / (res["mean_ms_per_call"] * 1e-3) / 1e12, 1)
+    res["tflops"] = round(n_cu * 2 * 4 * iters * per_iter * 32768 / (res["mean_ms_per_call"] * 1e-3) / 1e12, 1)
     return res
 
 
@@ -493,8 +498,20 @@ def measured_peaks(dev, stream, reps: int = 5) -> dict:
     mwg, iters = n_cu * 2, 20000  # two waves per SIMD, four independent MFMA chains each
     fsink = torch.empty(mwg * 256, dtype=torch.float32, device=dev)
     t_mfma = timed(lambda: pk.ba_peak_mfma_bf16(fsink.data_ptr(), mwg, iters, 2.0 ** -10, sptr))
-    del fsink
     mfma_tfs = mwg * 4 * iters * 4 * 32768 / t_mfma / 1e12
+    # random operands: the clock settles lower under their switching power, so
+    # the loop runs back to back for about half a second before it is timed
+    riters = 5000
+    rand = lambda: pk.ba_peak_mfma_bf16_random(fsink.data_ptr(), mwg, riters, 12345, sptr)
+    t_end = time.time() + 0.5
+    while time.time() < t_end:
+        for _ in range(20):
+            if rand() != 0:
+                raise RuntimeError("peak microbenchmark launch failed")
+        torch.cuda.synchronize()
+    t_rand = timed(rand)
+    del fsink
+    rand_tfs = mwg * 4 * riters * 8 * 32768 / t_rand / 1e12
     return {
         "hbm_read_tbs": round(nbytes / t_read[g_read] / 1e12, 3),
         "hbm_copy_tbs": round(2 * half / t_copy[g_copy] / 1e12, 3),
@@ -502,9 +519,14 @@ def measured_peaks(dev, stream, reps: int = 5) -> dict:
         "mfma_bf16_tflops": round(mfma_tfs, 1),
         # v_mfma_f32_32x32x16_bf16: 32768 FLOP per 32 cycles per SIMD, 4 SIMDs per CU
         "implied_clock_ghz": round(mfma_tfs * 1e12 / (n_cu * 4 * 1024) / 1e9, 3),
+        # the same loop on random bf16 operands (eight pairs per wave)
+        "mfma_bf16_random_operands_tflops": round(rand_tfs, 1),
+        "random_operands_implied_clock_ghz": round(rand_tfs * 1e12 / (n_cu * 4 * 1024) / 1e9, 3),
         "vendor": {"hbm_tbs": HBM_PEAK_GBS / 1000.0, "mfma_bf16_tflops": MFMA_BF16_PEAK_TFS},
         "workload": "read 4 GiB and copy 2 GiB (best of 2/8/32 workgroups per CU); "
-                    "2 waves per SIMD x 20000 rounds of 4 independent MFMAs",
+                    "2 waves per SIMD x 20000 rounds of 4 independent MFMAs on constant operands; "
+                    "2 waves per SIMD x 5000 rounds of 8 MFMAs over 8 random operand pairs, "
+                    "after 0.5 s back to back",
     }
 
 
@@ -754,7 +776,8 @@ def main():
     power = None
     if args.power:
         power = {"sparse": power_sample(P.sparse, stream, 4.0), "dense": power_sample(P.dense, stream, 4.0),
-                 "mfma_loop": mfma_loop_power(dev, stream, 4.0)}
+                 "mfma_loop": mfma_loop_power(dev, stream, 4.0),
+                 "mfma_loop_random_operands": mfma_loop_power(dev, stream, 4.0, random_operands=True)}
         print(f"[bench] power: {power}", file=sys.stderr, flush=True)
 
     # ---- the product path's own outputs for the parity check against the
@@ -845,7 +868,10 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel (sparse)",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
-                     "work_per_launch": kept_flops},
+                     "work_per_launch": kept_flops,
+                     # context: the MFMA-only loop on random operands, measured here
+                     "frac_of_random_operand_mfma_loop":
+                         round(achieved / peaks["mfma_bf16_random_operands_tflops"], 4) if peaks else None},
         "roofline_select": {"bound": "hbm", "kernel": "pool_stats_kernel + score_topk_kernel",
                             "achieved": round(sel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(sel_gbs / HBM_PEAK_GBS, 4), "traffic": sel_traffic,

@@ -58,6 +58,45 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(float* __restrict__ sink
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// 32-bit integer mixer (the finalizer of a multiply-xorshift hash): a
+// counter-based source of operand bits, so no memory is read in the loop
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+// random sign, exponent 2^-2 .. 2^2 and 7-bit mantissa
+__device__ __forceinline__ __bf16 random_bf16(uint32_t h) {
+  const uint32_t expo = 125u + (h >> 16) % 5u;
+  const uint16_t bits = (uint16_t)(((h & 1u) << 15) | (expo << 7) | ((h >> 8) & 0x7Fu));
+  return __builtin_bit_cast(__bf16, bits);
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_random_kernel(float* __restrict__ sink, int iters, uint32_t seed) {
+  bf16x8 a[8], b[8];
+  const uint32_t base = seed + (blockIdx.x * kThreads + threadIdx.x) * 128u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[i][e] = random_bf16(mix32(base + i * 8 + e));
+      b[i][e] = random_bf16(mix32(base + 64 + i * 8 + e));
+    }
+  f32x16 c[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], c[i & 3], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c[0][r] + c[1][r] + c[2][r] + c[3][r];
+  sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
 }  // namespace ba
 
 namespace {
@@ -90,6 +129,13 @@ int ba_peak_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, v
 int ba_peak_mfma_bf16(float* sink, int32_t workgroups, int32_t iters, float x, void* stream) {
   if (!sink || workgroups < 1 || iters < 1) return 1;
   ba::mfma_kernel<<<dim3((unsigned)workgroups), ba::kThreads, 0, static_cast<hipStream_t>(stream)>>>(sink, iters, x);
+  return finish();
+}
+
+int ba_peak_mfma_bf16_random(float* sink, int32_t workgroups, int32_t iters, uint32_t seed, void* stream) {
+  if (!sink || workgroups < 1 || iters < 1) return 1;
+  ba::mfma_random_kernel<<<dim3((unsigned)workgroups), ba::kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      sink, iters, seed);
   return finish();
 }
 

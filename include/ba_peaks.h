@@ -1,9 +1,10 @@
 /* Machine-peak microbenchmarks for the rooflines of libba_att.
  *
- * Not part of the attention operator: three kernels that confirm, on the GPU
- * the library runs on, the two constants its rooflines are priced against --
- * HBM bandwidth (streaming read, and copy) and the bf16 matrix-core rate --
- * next to the vendor's figures.  Built into libba_peaks.so.
+ * Not part of the attention operator: kernels that confirm, on the GPU the
+ * library runs on, the two constants its rooflines are priced against -- HBM
+ * bandwidth (streaming read, and copy) and the bf16 matrix-core rate -- next
+ * to the vendor's figures, and the matrix-core rate on random operands, whose
+ * switching power lowers the clock.  Built into libba_peaks.so.
  *
  * Conventions as in ba_att.h: device pointers, a hipStream_t passed as void*,
  * the caller owns every buffer, nothing is allocated, arguments are checked
@@ -34,6 +35,14 @@ int ba_peak_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, v
  * thread writes the sum of its accumulators to sink[workgroups*256].
  * FLOPs = workgroups * 4 * iters * 4 * 32768. */
 int ba_peak_mfma_bf16(float* sink, int32_t workgroups, int32_t iters, float x, void* stream);
+
+/* As ba_peak_mfma_bf16, but every wave cycles through eight different pairs
+ * of register operands, each element a bf16 with a random sign, a random
+ * exponent in [-2, 2] and a random 7-bit mantissa drawn from a hash of
+ * (seed, thread, element), like the values of attention's Q, K, V and P
+ * tiles; every iteration issues the eight products over four independent
+ * accumulators.  FLOPs = workgroups * 4 * iters * 8 * 32768. */
+int ba_peak_mfma_bf16_random(float* sink, int32_t workgroups, int32_t iters, uint32_t seed, void* stream);
 
 #ifdef __cplusplus
 }
