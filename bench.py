@@ -91,6 +91,10 @@ def parse():
     ap.add_argument("--power", action="store_true",
                     help="also sample socket power and graphics clocks (amd-smi) while the sparse kernel, "
                          "the dense kernel and the bf16 MFMA peak loop each run back to back for a few seconds")
+    ap.add_argument("--operand-data", action="store_true",
+                    help="also run the sparse and dense kernels, with the workload's own block lists, on "
+                         "zeros, ones, normals with 2-bit mantissas, normals and the workload's inputs, "
+                         "each back to back for a few seconds with power and clocks sampled")
     ap.add_argument("--skip-split", action="store_true",
                     help="omit the split key-list and external-contribution measurements")
     ap.add_argument("--skip-sweep", action="store_true",
@@ -460,6 +464,56 @@ def mfma_loop_power(dev, stream, seconds: float, random_operands: bool = False) 
     return res
 
 
+def operand_data(P, dev, stream, seconds: float = 3.0) -> dict:
+    """The sparse kernel (the workload's own block lists) and the dense kernel
+    on operands of decreasing bit activity: the same instructions, the same
+    memory traffic, only the values differ.  Each runs back to back while
+    power and clocks are sampled.  Normals are drawn on the GPU from a seeded
+    generator; the 2-bit variant keeps sign, exponent and the top two
+    mantissa bits of each bf16 normal."""
+    import torch
+    B, H, N, D, blk = P.dims
+    kept = kept_tile_flops(P.mask.cpu().numpy(), N, D, blk)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260)
+
+    def normals(bits_mask=None):
+        out = []
+        for _ in range(3):
+            t = torch.randn((B, H, N, D), generator=gen, device=dev).to(torch.bfloat16)
+            if bits_mask is not None:
+                t = (t.view(torch.int16) & bits_mask).view(torch.bfloat16)
+            out.append(t)
+        return out
+
+    own = (P.q, P.k, P.v)
+    variants = [("zeros", lambda: [torch.zeros((B, H, N, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]),
+                ("ones", lambda: [torch.ones((B, H, N, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]),
+                ("normal, 2-bit mantissa", lambda: normals(-32)),   # 0xFFE0
+                ("normal", normals),
+                ("workload inputs", lambda: list(own))]
+    res = {}
+    try:
+        for name, make in variants:
+            P.q, P.k, P.v = make()
+            row = {}
+            for kname, fn, fl in (("sparse", P.sparse, kept), ("dense", P.dense, P.dense_flops)):
+                r = power_sample(fn, stream, seconds)
+                ms = r["mean_ms_per_call"]
+                clocks = [c for smp in r["samples"] for c in smp["gfx_mhz"]]
+                row[kname] = {"ms": ms, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                              "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                              "socket_w": [smp["socket_w"] for smp in r["samples"]],
+                              "gfx_mhz_range": [min(clocks), max(clocks)] if clocks else None}
+            res[name] = row
+            print(f"[bench] operand data {name}: {row}", file=sys.stderr, flush=True)
+            P.q = P.k = P.v = None
+            torch.cuda.empty_cache()
+    finally:
+        P.q, P.k, P.v = own
+    return res
+
+
 def measured_peaks(dev, stream, reps: int = 5) -> dict:
     """HBM read and copy bandwidth and the bf16 MFMA rate measured on this GPU
     (libba_peaks.so), as context for the vendor peaks the rooflines use."""
@@ -779,6 +833,7 @@ def main():
                  "mfma_loop": mfma_loop_power(dev, stream, 4.0),
                  "mfma_loop_random_operands": mfma_loop_power(dev, stream, 4.0, random_operands=True)}
         print(f"[bench] power: {power}", file=sys.stderr, flush=True)
+    opdata = operand_data(P, dev, stream) if args.operand_data else None
 
     # ---- the product path's own outputs for the parity check against the
     # oracle: the forward on the GPU's block lists with fp32 output
@@ -883,6 +938,7 @@ def main():
         "split_kv": split_kv,
         "external": external,
         "power": power,
+        "operand_data": opdata,
         "selection_quality": quality,
         # the pages' only operator-speed figure, as context: it names no hardware,
         # sequence length or sparsity, so it is no target for this measurement
