@@ -543,12 +543,15 @@ def measured_peaks(dev, stream, reps: int = 5) -> dict:
     nbytes = 4 << 30  # far beyond the 256 MB MALL: every byte comes from HBM
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     half = nbytes // 2
-    t_read = {g: timed(lambda: pk.ba_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), n_cu * g, sptr))
+    t_read = {g: timed(lambda: pk.ba_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), n_cu * g, 0, sptr))
               for g in grids}
+    t_read_nt = {g: timed(lambda: pk.ba_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), n_cu * g, 1, sptr))
+                 for g in grids}
     t_copy = {g: timed(lambda: pk.ba_peak_copy(buf.data_ptr(), buf.data_ptr() + half, half, n_cu * g, sptr))
               for g in grids}
     del buf, sink
     g_read, g_copy = min(t_read, key=t_read.get), min(t_copy, key=t_copy.get)
+    g_read_nt = min(t_read_nt, key=t_read_nt.get)
     mwg, iters = n_cu * 2, 20000  # two waves per SIMD, four independent MFMA chains each
     fsink = torch.empty(mwg * 256, dtype=torch.float32, device=dev)
     t_mfma = timed(lambda: pk.ba_peak_mfma_bf16(fsink.data_ptr(), mwg, iters, 2.0 ** -10, sptr))
@@ -568,8 +571,9 @@ def measured_peaks(dev, stream, reps: int = 5) -> dict:
     rand_tfs = mwg * 4 * riters * 8 * 32768 / t_rand / 1e12
     return {
         "hbm_read_tbs": round(nbytes / t_read[g_read] / 1e12, 3),
+        "hbm_read_nontemporal_tbs": round(nbytes / t_read_nt[g_read_nt] / 1e12, 3),
         "hbm_copy_tbs": round(2 * half / t_copy[g_copy] / 1e12, 3),
-        "workgroups_per_cu": {"read": g_read, "copy": g_copy},
+        "workgroups_per_cu": {"read": g_read, "read_nontemporal": g_read_nt, "copy": g_copy},
         "mfma_bf16_tflops": round(mfma_tfs, 1),
         # v_mfma_f32_32x32x16_bf16: 32768 FLOP per 32 cycles per SIMD, 4 SIMDs per CU
         "implied_clock_ghz": round(mfma_tfs * 1e12 / (n_cu * 4 * 1024) / 1e9, 3),
@@ -577,7 +581,8 @@ def measured_peaks(dev, stream, reps: int = 5) -> dict:
         "mfma_bf16_random_operands_tflops": round(rand_tfs, 1),
         "random_operands_implied_clock_ghz": round(rand_tfs * 1e12 / (n_cu * 4 * 1024) / 1e9, 3),
         "vendor": {"hbm_tbs": HBM_PEAK_GBS / 1000.0, "mfma_bf16_tflops": MFMA_BF16_PEAK_TFS},
-        "workload": "read 4 GiB and copy 2 GiB (best of 2/8/32 workgroups per CU); "
+        "workload": "read 4 GiB with plain and with nontemporal loads and copy 2 GiB (best of 2/8/32 "
+                    "workgroups per CU); "
                     "2 waves per SIMD x 20000 rounds of 4 independent MFMAs on constant operands; "
                     "2 waves per SIMD x 5000 rounds of 8 MFMAs over 8 random operand pairs, "
                     "after 0.5 s back to back",

@@ -65,7 +65,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
 # the rooflines' context only
 PEAKS_PATH = os.path.join(_PKG, "libba_peaks.so")
 PEAK_SIGNATURES = [
-    ("ba_peak_read", ctypes.c_int, [_p, _sz, _p, _i32, _p]),
+    ("ba_peak_read", ctypes.c_int, [_p, _sz, _p, _i32, _i32, _p]),
     ("ba_peak_copy", ctypes.c_int, [_p, _p, _sz, _i32, _p]),
     ("ba_peak_mfma_bf16", ctypes.c_int, [_p, _i32, _i32, _f32, _p]),
     ("ba_peak_mfma_bf16_random", ctypes.c_int, [_p, _i32, _i32, ctypes.c_uint32, _p]),

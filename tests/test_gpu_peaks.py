@@ -19,15 +19,15 @@ def peaks(gpu_lib):
     return _lib.load_peaks(), torch.cuda.current_stream().cuda_stream
 
 
-@pytest.mark.parametrize("nbytes,groups", [(16, 1), (4096, 2), ((1 << 20) + 48, 5)])
-def test_read_digest_and_copy(peaks, nbytes, groups):
+@pytest.mark.parametrize("nbytes,groups,nt", [(16, 1, 0), (4096, 2, 1), ((1 << 20) + 48, 5, 0), ((1 << 20) + 48, 7, 1)])
+def test_read_digest_and_copy(peaks, nbytes, groups, nt):
     import torch
     pk, s = peaks
     rng = np.random.default_rng(nbytes)
     host = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
     src = torch.from_numpy(host.view(np.int32)).cuda()
     sink = torch.zeros(groups * 256, dtype=torch.int32, device="cuda")
-    assert pk.ba_peak_read(src.data_ptr(), nbytes, sink.data_ptr(), groups, s) == 0
+    assert pk.ba_peak_read(src.data_ptr(), nbytes, sink.data_ptr(), groups, nt, s) == 0
     dst = torch.zeros_like(src)
     assert pk.ba_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, groups, s) == 0
     torch.cuda.synchronize()
