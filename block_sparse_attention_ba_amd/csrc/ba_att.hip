@@ -95,7 +95,7 @@ int score_rows(int BH, int n, int D, int NI) {
     for (int R : {64, 32, 16}) {
       if ((R == 64 && NI > 4) || (R == 32 && NI > 16)) continue;
       const int ctw = NI >= 4 ? NI / 4 : 1;
-      if ((R / 16) * ctw > 8 || ba::score_lds_bytes(D, R, n) > ba::kScoreLdsBytes) continue;
+      if ((R / 16) * ctw > 8 || cover * ba::score_lds_bytes(D, R, n) > ba::kScoreLdsBytes) continue;
       if ((long long)BH * ((n + R - 1) / R) >= (long long)cover * cus) return R;
     }
   }

@@ -316,10 +316,35 @@ __device__ __forceinline__ void radix_select_rows(const uint32_t (&key)[P][NI], 
   }
 }
 
-// LDS bytes of one score workgroup: the A tile [R][3D] (fp32) while the
-// products run, then, in the same memory, the score rows [R][n + 4].
+// LDS bytes of one score workgroup: the A tile as three bf16 planes
+// [3][R][3D] while the products run, then, in the same memory, the score
+// rows [R][n + 4] (fp32).
 __host__ __device__ constexpr int score_lds_bytes(int D, int R, int n) {
-  return (3 * D > n + 4 ? R * 3 * D : R * (n + 4)) * 4;
+  return 3 * R * 3 * D * 2 > R * (n + 4) * 4 ? 3 * R * 3 * D * 2 : R * (n + 4) * 4;
+}
+
+// An fp32 value as the sum of three bf16, h + m + l: h rounds x, m rounds
+// the remainder x - h, l the remainder after m.  Each remainder is exact in
+// fp32, so the three carry x's 24 significant bits.
+__device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+  h = (__bf16)x;
+  const float r1 = x - (float)h;
+  m = (__bf16)r1;
+  l = (__bf16)(r1 - (float)m);
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// eight values, lo then hi
+__device__ __forceinline__ void split3(const f32x4 lo, const f32x4 hi, bf16x8& h, bf16x8& m, bf16x8& l) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 a, b, c;
+    split3(e < 4 ? lo[e] : hi[e - 4], a, b, c);
+    h[e] = a;
+    m[e] = b;
+    l[e] = c;
+  }
 }
 
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3): loads past
@@ -334,29 +359,35 @@ __device__ __forceinline__ f32x4 load_f32x4(__amdgpu_buffer_rsrc_t rs, int byte_
 
 // Rows R0 .. R0+R-1 of head bh, by a workgroup of W waves whose LDS starts at lds.
 //
-// The whole A tile (aq rows) is staged in LDS with every load in flight
-// before the first write; the B operand (ak) streams through registers, PF
-// float4 loads ahead of the MFMAs that use them.  Buffer loads return zero
-// past row/column n, so no load is predicated and the compiler can wait for
-// each one by count instead of for all of them.
+// S = aq . ak^T is formed on the bf16 matrix cores: each fp32 operand is the
+// sum of three bf16 (split3), and the six products of pieces down to
+// 2^-24 relative are summed, smallest first, into fp32 accumulators -- the
+// accuracy of an fp32 product at 6/16 of its matrix-core time.  The whole A
+// tile (aq rows) is split once into three bf16 planes in LDS, with every
+// load in flight before the first write; the B operand (ak) streams through
+// registers, PF K steps ahead of the MFMAs that use it, and is split there.
+// Buffer loads return zero past row/column n, so no load is predicated and
+// the compiler can wait for each one by count instead of for all of them.
 template <int D, int NI, int R, int W>
 __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const float* __restrict__ ak, int n,
                                            int keep, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
                                            int32_t* __restrict__ cnt, float* __restrict__ score, int bh, int R0,
                                            float* lds) {
   constexpr int K3 = 3 * D;
-  constexpr int F4 = K3 / 4;          // float4 slots per A row
-  constexpr int SWZ = 15;             // slot swizzle within aligned groups of 16 slots
-  static_assert(F4 % (SWZ + 1) == 0, "swizzle must stay inside the row");
-  constexpr int KS = K3 / 16;         // K steps: one float4 of B per lane and step
+  constexpr int F4 = K3 / 4;          // float4 slots per A row (fp32)
+  constexpr int F8 = K3 / 8;          // 16-byte slots per A row and plane (bf16)
+  constexpr int SWZ = F8 % 16 == 0 ? 15 : 7;  // slot swizzle within aligned groups of SWZ + 1 slots
+  static_assert(F8 % (SWZ + 1) == 0, "swizzle must stay inside the row");
+  constexpr int KS = K3 / 32;         // K steps: eight values of B per lane and step
   constexpr int RT = R / 16;          // row tiles
   constexpr int CTW = (4 * NI + W - 1) / W;  // column tiles per wave (4*NI tiles cover 64*NI columns)
   constexpr int STEPS = CTW * KS;
-  constexpr int PF = STEPS < 8 ? STEPS : 8;  // B loads in flight per lane
+  constexpr int PF = STEPS < 2 ? STEPS : 2;  // B steps in flight per lane
   constexpr int T = W * 64;
   constexpr int AL = (R * F4 + T - 1) / T;  // A float4 loads per thread
+  constexpr int PLANE = R * K3;             // bf16 elements per plane
   static_assert(RT * CTW <= 8, "accumulators of a wave");
-  float* const Abuf = lds;  // [R][K3], float4 slot j of row r at j ^ (r & SWZ)
+  __bf16* const Abuf = reinterpret_cast<__bf16*>(lds);  // [3][R][K3]; slot j of row r at j ^ (r & SWZ)
   float* const Sbuf = lds;  // [R][SP], once every wave is done with Abuf
   const int SP = n + 4;
 
@@ -368,24 +399,39 @@ __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const f
   const auto a_rs = score_rsrc(aq + ((size_t)bh * n + R0) * K3, rows_here * K3 * 4);
   const auto b_rs = score_rsrc(ak + (size_t)bh * n * K3, n * K3 * 4);
   // step s = (column tile t of this wave, K step m); lane (li, lg) takes
-  // k = 16m + 4lg + e for MFMA e of the step in both operands
+  // k = 32m + 8lg + e for element e of the step in both operands
   auto b_offset = [&](int s) {
     const int t = s / KS, m = s - t * KS;
-    return (((wave + W * t) * 16 + li) * K3 + 16 * m + 4 * lg) * 4;
+    return (((wave + W * t) * 16 + li) * K3 + 32 * m + 8 * lg) * 4;
   };
 
   f32x4 av[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) av[i] = load_f32x4(a_rs, (threadIdx.x + i * T) * 16);
-  f32x4 b[PF];
+  f32x4 b[PF][2];
 #pragma unroll
-  for (int s = 0; s < PF; ++s) b[s] = load_f32x4(b_rs, b_offset(s));
+  for (int s = 0; s < PF; ++s) {
+    b[s][0] = load_f32x4(b_rs, b_offset(s));
+    b[s][1] = load_f32x4(b_rs, b_offset(s) + 16);
+  }
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
     const int e = threadIdx.x + i * T;
     if ((R * F4) % T == 0 || e < R * F4) {
-      const int row = e / F4, j = e - row * F4;
-      *reinterpret_cast<f32x4*>(Abuf + row * K3 + 4 * (j ^ (row & SWZ))) = av[i];
+      const int row = e / F4, j = e - row * F4;  // values 4j .. 4j+3 of the row: half j & 1 of slot j >> 1
+      const int off = row * K3 + 8 * ((j >> 1) ^ (row & SWZ)) + 4 * (j & 1);
+      bf16x4 h, m, l;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __bf16 a, b, c;
+        split3(av[i][q], a, b, c);
+        h[q] = a;
+        m[q] = b;
+        l[q] = c;
+      }
+      *reinterpret_cast<bf16x4*>(Abuf + off) = h;
+      *reinterpret_cast<bf16x4*>(Abuf + PLANE + off) = m;
+      *reinterpret_cast<bf16x4*>(Abuf + 2 * PLANE + off) = l;
     }
   }
   __syncthreads();
@@ -399,20 +445,39 @@ __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const f
   for (int s = 0; s < STEPS; ++s) {
     const int t = s / KS, m = s - t * KS;
     if (wave + W * t < ctiles) {
-      f32x4 a[RT];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
+      bf16x8 bh, bm, bl;
+      split3(b[s % PF][0], b[s % PF][1], bh, bm, bl);
+      // the six piece products, smallest first, each A plane read just before
+      // its products; row tiles innermost, so that consecutive MFMAs of a
+      // wave use different accumulators
+      auto plane = [&](int p, int r) {
         const int row = r * 16 + li;
-        a[r] = *reinterpret_cast<const f32x4*>(Abuf + row * K3 + 4 * ((4 * m + lg) ^ (row & SWZ)));
-      }
-      // row tiles innermost: consecutive MFMAs of a wave use different accumulators
+        return *reinterpret_cast<const bf16x8*>(Abuf + p * PLANE + row * K3 + 8 * ((4 * m + lg) ^ (row & SWZ)));
+      };
+      bf16x8 a[RT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int r = 0; r < RT; ++r) a[r] = plane(2, r);
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
-          acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r][e], b[s % PF][e], acc[t][r], 0, 0, 0);
+      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) a[r] = plane(1, r);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bm, acc[t][r], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) a[r] = plane(0, r);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bl, acc[t][r], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bm, acc[t][r], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
     }
-    if (s + PF < STEPS) b[s % PF] = load_f32x4(b_rs, b_offset(s + PF));
+    if (s + PF < STEPS) {
+      b[s % PF][0] = load_f32x4(b_rs, b_offset(s + PF));
+      b[s % PF][1] = load_f32x4(b_rs, b_offset(s + PF) + 16);
+    }
   }
   __syncthreads();  // the score rows overwrite the A tile
   // lane holds column ct*16 + li of rows r*16 + 4*lg + {0..3}
