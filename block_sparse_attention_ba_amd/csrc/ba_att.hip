@@ -150,8 +150,8 @@ void launch_attn(const ba::AttnParams& p, bool out_f32, hipStream_t s) {
 }
 
 // Workspace of the selection pass: the pooled statistics aq, ak (fp32
-// [B*H, n, 3D] each).
-size_t select_workspace_bytes(int BH, int n, int D) { return 2 * (size_t)BH * n * 3 * D * sizeof(float); }
+// [B*H, n, 2D] each).
+size_t select_workspace_bytes(int BH, int n, int D) { return 2 * (size_t)BH * n * 2 * D * sizeof(float); }
 
 // Checks of ba_att_select's arguments other than its workspace.
 ba_status check_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, double sparsity,
@@ -169,8 +169,8 @@ ba_status check_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block
   return BA_OK;
 }
 
-// The selection pass with the pooled statistics at ws: aq [B*H, n, 3D] then
-// ak [B*H, n, 3D], fp32 (checked arguments).
+// The selection pass with the pooled statistics at ws: aq [B*H, n, 2D] then
+// ak [B*H, n, 2D], fp32 (checked arguments).
 ba_status launch_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
                         double sparsity, const void* q, const void* k, uint8_t* block_mask,
                         int32_t* block_idx, int32_t* block_cnt, float* score, float* ws, hipStream_t s) {
@@ -179,7 +179,7 @@ ba_status launch_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bloc
   const int BH = B * H;
   const float sc = resolve_scale(scale, D);
   float* aq = ws;
-  float* ak = aq + (size_t)BH * n * 3 * D;
+  float* ak = aq + (size_t)BH * n * 2 * D;
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   if (D == 128) {

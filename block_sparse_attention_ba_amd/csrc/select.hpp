@@ -121,25 +121,21 @@ __device__ __forceinline__ void pool_block(const uint16_t* __restrict__ q, const
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = xor_sum(s[e], m);
 
+  // stored: aq = [scale * mean, scale^2 / 2 * var], ak = [mean, var]; the
+  // third segment of each augmented vector follows from these two and is
+  // formed by the score kernel
   if (rg == 0) {
-    float* out = (tensor == 0 ? aq : ak) + ((size_t)bh * n + I) * (3 * D) + c * 8;
-    f32x4 seg[3][2];
+    float* out = (tensor == 0 ? aq : ak) + ((size_t)bh * n + I) * (2 * D) + c * 8;
+    f32x4 seg[2][2];
     const float hs2 = 0.5f * scale * scale;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float var = s[e] * inv_rows;
-      if (tensor == 0) {
-        seg[0][e / 4][e % 4] = scale * mean[e];
-        seg[1][e / 4][e % 4] = hs2 * var;
-        seg[2][e / 4][e % 4] = hs2 * (mean[e] * mean[e]);
-      } else {
-        seg[0][e / 4][e % 4] = mean[e];
-        seg[1][e / 4][e % 4] = var + mean[e] * mean[e];
-        seg[2][e / 4][e % 4] = var;
-      }
+      seg[0][e / 4][e % 4] = tensor == 0 ? scale * mean[e] : mean[e];
+      seg[1][e / 4][e % 4] = tensor == 0 ? hs2 * var : var;
     }
 #pragma unroll
-    for (int g = 0; g < 3; ++g) {
+    for (int g = 0; g < 2; ++g) {
       reinterpret_cast<f32x4*>(out + g * D)[0] = seg[g][0];
       reinterpret_cast<f32x4*>(out + g * D)[1] = seg[g][1];
     }
@@ -359,30 +355,34 @@ __device__ __forceinline__ f32x4 load_f32x4(__amdgpu_buffer_rsrc_t rs, int byte_
 
 // Rows R0 .. R0+R-1 of head bh, by a workgroup of W waves whose LDS starts at lds.
 //
-// S = aq . ak^T is formed on the bf16 matrix cores: each fp32 operand is the
-// sum of three bf16 (split3), and the six products of pieces down to
-// 2^-24 relative are summed, smallest first, into fp32 accumulators -- the
-// accuracy of an fp32 product at 6/16 of its matrix-core time.  The whole A
-// tile (aq rows) is split once into three bf16 planes in LDS, with every
-// load in flight before the first write; the B operand (ak) streams through
-// registers, PF K steps ahead of the MFMAs that use it, and is split there.
-// Buffer loads return zero past row/column n, so no load is predicated and
-// the compiler can wait for each one by count instead of for all of them.
+// S = A . B^T over the augmented 3D-vectors A = [aq0, aq1, aq0^2 / 2] and
+// B = [ak0, ak1 + ak0^2, ak1], from the two stored segments of aq and ak.  It
+// is formed on the bf16 matrix cores: each fp32 operand is the sum of three
+// bf16 (split3), and the six products of pieces down to 2^-24 relative are
+// summed, smallest first, into fp32 accumulators -- the accuracy of an fp32
+// product at 6/16 of its matrix-core time.  The whole A tile is formed and
+// split once into three bf16 planes in LDS, with every load in flight before
+// the first write.  B streams through registers in 32-wide blocks of d: a
+// block's two stored segments give all three of its augmented segments,
+// each split as it is used, and each stored segment's registers take the
+// next block's loads as soon as its last use is split.  Buffer loads return zero
+// past row/column n, so no load is predicated and the compiler can wait for
+// each one by count instead of for all of them.
 template <int D, int NI, int R, int W>
 __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const float* __restrict__ ak, int n,
                                            int keep, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
                                            int32_t* __restrict__ cnt, float* __restrict__ score, int bh, int R0,
                                            float* lds) {
-  constexpr int K3 = 3 * D;
-  constexpr int F4 = K3 / 4;          // float4 slots per A row (fp32)
+  constexpr int K2 = 2 * D;           // stored values per row
+  constexpr int K3 = 3 * D;           // augmented values per row
+  constexpr int F4 = K2 / 4;          // float4 slots per stored A row
   constexpr int F8 = K3 / 8;          // 16-byte slots per A row and plane (bf16)
   constexpr int SWZ = F8 % 16 == 0 ? 15 : 7;  // slot swizzle within aligned groups of SWZ + 1 slots
   static_assert(F8 % (SWZ + 1) == 0, "swizzle must stay inside the row");
-  constexpr int KS = K3 / 32;         // K steps: eight values of B per lane and step
+  constexpr int DB = D / 32;          // 32-wide blocks of d: eight values per lane and segment
   constexpr int RT = R / 16;          // row tiles
   constexpr int CTW = (4 * NI + W - 1) / W;  // column tiles per wave (4*NI tiles cover 64*NI columns)
-  constexpr int STEPS = CTW * KS;
-  constexpr int PF = STEPS < 2 ? STEPS : 2;  // B steps in flight per lane
+  constexpr int STEPS = CTW * DB;
   constexpr int T = W * 64;
   constexpr int AL = (R * F4 + T - 1) / T;  // A float4 loads per thread
   constexpr int PLANE = R * K3;             // bf16 elements per plane
@@ -396,42 +396,50 @@ __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const f
   const int li = lane & 15, lg = lane >> 4;
   const int ctiles = (n + 15) / 16;
   const int rows_here = min(R, n - R0);
-  const auto a_rs = score_rsrc(aq + ((size_t)bh * n + R0) * K3, rows_here * K3 * 4);
-  const auto b_rs = score_rsrc(ak + (size_t)bh * n * K3, n * K3 * 4);
-  // step s = (column tile t of this wave, K step m); lane (li, lg) takes
-  // k = 32m + 8lg + e for element e of the step in both operands
+  const auto a_rs = score_rsrc(aq + ((size_t)bh * n + R0) * K2, rows_here * K2 * 4);
+  const auto b_rs = score_rsrc(ak + (size_t)bh * n * K2, n * K2 * 4);
+  // step s = (column tile t of this wave, d block m); lane (li, lg) takes
+  // d = 32m + 8lg + e for element e, in both operands and every segment
   auto b_offset = [&](int s) {
-    const int t = s / KS, m = s - t * KS;
-    return (((wave + W * t) * 16 + li) * K3 + 32 * m + 8 * lg) * 4;
+    const int t = s / DB, m = s - t * DB;
+    return (((wave + W * t) * 16 + li) * K2 + 32 * m + 8 * lg) * 4;
+  };
+  // the eight values of stored segment g (ak0 or ak1) for step s
+  auto load_b = [&](int s, int g, f32x4 (&dst)[2]) {
+    const int o = b_offset(s) + g * 4 * D;
+    dst[0] = load_f32x4(b_rs, o);
+    dst[1] = load_f32x4(b_rs, o + 16);
+  };
+  // three bf16 planes of the augmented value v at augmented index k of row
+  auto put_a = [&](int row, int k, const f32x4 v) {
+    const int off = row * K3 + 8 * ((k >> 3) ^ (row & SWZ)) + (k & 7);
+    bf16x4 h, m, l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __bf16 a, b, c;
+      split3(v[q], a, b, c);
+      h[q] = a;
+      m[q] = b;
+      l[q] = c;
+    }
+    *reinterpret_cast<bf16x4*>(Abuf + off) = h;
+    *reinterpret_cast<bf16x4*>(Abuf + PLANE + off) = m;
+    *reinterpret_cast<bf16x4*>(Abuf + 2 * PLANE + off) = l;
   };
 
   f32x4 av[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) av[i] = load_f32x4(a_rs, (threadIdx.x + i * T) * 16);
-  f32x4 b[PF][2];
-#pragma unroll
-  for (int s = 0; s < PF; ++s) {
-    b[s][0] = load_f32x4(b_rs, b_offset(s));
-    b[s][1] = load_f32x4(b_rs, b_offset(s) + 16);
-  }
+  f32x4 x0[2], x1[2];  // ak0 and ak1 of the current block
+  load_b(0, 0, x0);
+  load_b(0, 1, x1);
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
     const int e = threadIdx.x + i * T;
     if ((R * F4) % T == 0 || e < R * F4) {
-      const int row = e / F4, j = e - row * F4;  // values 4j .. 4j+3 of the row: half j & 1 of slot j >> 1
-      const int off = row * K3 + 8 * ((j >> 1) ^ (row & SWZ)) + 4 * (j & 1);
-      bf16x4 h, m, l;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        __bf16 a, b, c;
-        split3(av[i][q], a, b, c);
-        h[q] = a;
-        m[q] = b;
-        l[q] = c;
-      }
-      *reinterpret_cast<bf16x4*>(Abuf + off) = h;
-      *reinterpret_cast<bf16x4*>(Abuf + PLANE + off) = m;
-      *reinterpret_cast<bf16x4*>(Abuf + 2 * PLANE + off) = l;
+      const int row = e / F4, k = 4 * (e - row * F4);  // stored values k .. k+3 of the row
+      put_a(row, k, av[i]);                            // aq0 or aq1 at the same index
+      if (k < D) put_a(row, 2 * D + k, av[i] * av[i] * 0.5f);  // aq0^2 / 2
     }
   }
   __syncthreads();
@@ -441,43 +449,56 @@ __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const f
   for (int t = 0; t < CTW; ++t)
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the six piece products of augmented segment g of this block, smallest
+  // first, each A plane read just before its products; row tiles innermost,
+  // so that consecutive MFMAs of a wave use different accumulators
+  auto products = [&](int t, int m, int g, const bf16x8& bh, const bf16x8& bm, const bf16x8& bl) {
+    const int slot = g * (D / 8) + 4 * m + lg;
+    auto plane = [&](int p, int r) {
+      const int row = r * 16 + li;
+      return *reinterpret_cast<const bf16x8*>(Abuf + p * PLANE + row * K3 + 8 * (slot ^ (row & SWZ)));
+    };
+    bf16x8 a[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) a[r] = plane(2, r);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) a[r] = plane(1, r);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bm, acc[t][r], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) a[r] = plane(0, r);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bl, acc[t][r], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bm, acc[t][r], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
+  };
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int t = s / KS, m = s - t * KS;
-    if (wave + W * t < ctiles) {
-      bf16x8 bh, bm, bl;
-      split3(b[s % PF][0], b[s % PF][1], bh, bm, bl);
-      // the six piece products, smallest first, each A plane read just before
-      // its products; row tiles innermost, so that consecutive MFMAs of a
-      // wave use different accumulators
-      auto plane = [&](int p, int r) {
-        const int row = r * 16 + li;
-        return *reinterpret_cast<const bf16x8*>(Abuf + p * PLANE + row * K3 + 8 * ((4 * m + lg) ^ (row & SWZ)));
-      };
-      bf16x8 a[RT];
+    const int t = s / DB, m = s - t * DB;
+    const bool on = wave + W * t < ctiles;
+    bf16x8 bh, bm, bl;
+    // segment 0: ak0
+    split3(x0[0], x0[1], bh, bm, bl);
+    if (on) products(t, m, 0, bh, bm, bl);
+    // segment 1: ak1 + ak0^2, formed in ak0's registers, which then take the
+    // next block's ak0
 #pragma unroll
-      for (int r = 0; r < RT; ++r) a[r] = plane(2, r);
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) a[r] = plane(1, r);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bm, acc[t][r], 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) a[r] = plane(0, r);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bl, acc[t][r], 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bm, acc[t][r], 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) acc[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bh, acc[t][r], 0, 0, 0);
-    }
-    if (s + PF < STEPS) {
-      b[s % PF][0] = load_f32x4(b_rs, b_offset(s + PF));
-      b[s % PF][1] = load_f32x4(b_rs, b_offset(s + PF) + 16);
-    }
+      for (int q = 0; q < 4; ++q) x0[h2][q] = __builtin_fmaf(x0[h2][q], x0[h2][q], x1[h2][q]);
+    split3(x0[0], x0[1], bh, bm, bl);
+    if (s + 1 < STEPS) load_b(s + 1, 0, x0);
+    if (on) products(t, m, 1, bh, bm, bl);
+    // segment 2: ak1, whose registers then take the next block's ak1
+    split3(x1[0], x1[1], bh, bm, bl);
+    if (s + 1 < STEPS) load_b(s + 1, 1, x1);
+    if (on) products(t, m, 2, bh, bm, bl);
   }
   __syncthreads();  // the score rows overwrite the A tile
   // lane holds column ct*16 + li of rows r*16 + 4*lg + {0..3}

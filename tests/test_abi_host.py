@@ -63,8 +63,8 @@ def test_keep_count_matches_oracle_bit_exactly(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.ba_att_select_workspace_bytes(1, 32, 8192, 128, 64) == 2 * 32 * 128 * 384 * 4
-    assert lib.ba_att_select_workspace_bytes(1, 40, 32760, 128, 128) == 2 * 40 * 256 * 384 * 4
+    assert lib.ba_att_select_workspace_bytes(1, 32, 8192, 128, 64) == 2 * 32 * 128 * 256 * 4
+    assert lib.ba_att_select_workspace_bytes(1, 40, 32760, 128, 128) == 2 * 40 * 256 * 256 * 4
     assert lib.ba_att_select_workspace_bytes(1, 1, 1024, 96, 64) == 0
 
 
@@ -282,9 +282,9 @@ def test_select_noalloc_rejects_before_launch(lib):
 
     assert call(q=None) == 1 and call(sp=1.0) == 1 and call(q=FAKE + 2) == 1
     assert call(D=96) == 2 and call(block=32) == 2 and call(N=2049 * 64) == 2
-    # 2*64*1024*384*4 bytes of statistics: beyond the scratch
+    # 2*64*1024*256*4 bytes of statistics: beyond the scratch
     assert lib.ba_att_select_workspace_bytes(2, 32, 65536, 128, 64) > (64 << 20)
     assert call(B=2, H=32, N=65536, D=128, block=64) == 5
-    # the distribution-shift shape (B2 H32 N32768 D128 b128) fits: 48 MiB
-    assert lib.ba_att_select_workspace_bytes(2, 32, 32768, 128, 128) == 48 << 20
+    # the distribution-shift shape (B2 H32 N32768 D128 b128) fits: 32 MiB
+    assert lib.ba_att_select_workspace_bytes(2, 32, 32768, 128, 128) == 32 << 20
     assert b"scratch" in lib.ba_att_status_string(5)

@@ -86,17 +86,21 @@ def test_select_matches_oracle(gpu_lib, case):
 
     # pooled statistics in the caller's workspace: [aq | ak], 3D fp32 per block
     aw = ws.view(torch.float32).cpu().numpy().astype(np.float64)
-    aq = aw[: B * H * n * 3 * D].reshape(B, H, n, 3 * D)
-    ak = aw[B * H * n * 3 * D: 2 * B * H * n * 3 * D].reshape(B, H, n, 3 * D)
+    # stored statistics: aq = [scale * mean_q, scale^2 / 2 * var_q], ak = [mean_k, var_k]
+    aq = aw[: B * H * n * 2 * D].reshape(B, H, n, 2 * D)
+    ak = aw[B * H * n * 2 * D: 2 * B * H * n * 2 * D].reshape(B, H, n, 2 * D)
     sc = 1 / math.sqrt(D)
     assert np.allclose(aq[..., :D], sc * ref["qm"], rtol=1e-5, atol=1e-6)
-    assert np.allclose(aq[..., D:2 * D], 0.5 * sc * sc * ref["qv"], rtol=1e-4, atol=1e-7)
+    assert np.allclose(aq[..., D:], 0.5 * sc * sc * ref["qv"], rtol=1e-4, atol=1e-7)
     assert np.allclose(ak[..., :D], ref["km"], rtol=1e-5, atol=1e-6)
-    assert np.allclose(ak[..., 2 * D:], ref["kv"], rtol=1e-4, atol=1e-6)
+    assert np.allclose(ak[..., D:], ref["kv"], rtol=1e-4, atol=1e-6)
 
-    # score map: fp32 dot of 3D terms; bound by a few ulps of the sum of |terms|
+    # score map: fp32 dot of the augmented 3D terms [aq0, aq1, aq0^2/2] .
+    # [ak0, ak1 + ak0^2, ak1]; bound by a few ulps of the sum of |terms|
     S = ref["S"]
-    mag = np.einsum("bhic,bhjc->bhij", np.abs(aq), np.abs(ak))
+    aq3 = np.concatenate([aq[..., :D], aq[..., D:], 0.5 * aq[..., :D] ** 2], axis=-1)
+    ak3 = np.concatenate([ak[..., :D], ak[..., D:] + ak[..., :D] ** 2, ak[..., D:]], axis=-1)
+    mag = np.einsum("bhic,bhjc->bhij", np.abs(aq3), np.abs(ak3))
     err = np.abs(score - S)
     assert np.all(err <= 4e-5 * mag + 1e-7), float((err / (mag + 1e-30)).max())
 
