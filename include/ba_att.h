@@ -80,7 +80,7 @@ int32_t ba_att_num_blocks(int32_t N, int32_t block);
 int32_t ba_att_keep_count(int32_t n_blocks, double sparsity);
 
 /* Bytes of device workspace ba_att_select needs: the pooled block statistics
- * of Q and K, 2 * B*H*n * 3*D fp32.  Returns 0 for invalid sizes.  (A helper
+ * of Q and K, 2 * B*H*n * 2*D fp32.  Returns 0 for invalid sizes.  (A helper
  * of this interface; the pages define no workspace.) */
 size_t ba_att_select_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block);
 
