@@ -359,15 +359,16 @@ __device__ __forceinline__ f32x4 load_f32x4(__amdgpu_buffer_rsrc_t rs, int byte_
 // B = [ak0, ak1 + ak0^2, ak1], from the two stored segments of aq and ak.  It
 // is formed on the bf16 matrix cores: each fp32 operand is the sum of three
 // bf16 (split3), and the six products of pieces down to 2^-24 relative are
-// summed, smallest first, into fp32 accumulators -- the accuracy of an fp32
-// product at 6/16 of its matrix-core time.  The whole A tile is formed and
+// summed into fp32 accumulators (l.h, m.m, m.h, h.l, h.m, h.h: the two
+// smallest first, the largest last) -- the accuracy of an fp32 product at
+// 6/16 of its matrix-core time.  The whole A tile is formed and
 // split once into three bf16 planes in LDS, with every load in flight before
 // the first write.  B streams through registers in 32-wide blocks of d: a
 // block's two stored segments give all three of its augmented segments,
 // each split as it is used, and each stored segment's registers take the
-// next block's loads as soon as its last use is split.  Buffer loads return zero
-// past row/column n, so no load is predicated and the compiler can wait for
-// each one by count instead of for all of them.
+// next block's loads as soon as its last use is split.  Buffer loads return
+// zero past row/column n, so no load is predicated and the compiler can wait
+// for each one by count instead of for all of them.
 template <int D, int NI, int R, int W>
 __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const float* __restrict__ ak, int n,
                                            int keep, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
@@ -449,9 +450,10 @@ __device__ __forceinline__ void score_tile(const float* __restrict__ aq, const f
   for (int t = 0; t < CTW; ++t)
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the six piece products of augmented segment g of this block, smallest
-  // first, each A plane read just before its products; row tiles innermost,
-  // so that consecutive MFMAs of a wave use different accumulators
+  // the six piece products of augmented segment g of this block (l.h, m.m,
+  // m.h, h.l, h.m, h.h), each A plane read just before its products; row
+  // tiles innermost, so that consecutive MFMAs of a wave use different
+  // accumulators
   auto products = [&](int t, int m, int g, const bf16x8& bh, const bf16x8& bm, const bf16x8& bl) {
     const int slot = g * (D / 8) + 4 * m + lg;
     auto plane = [&](int p, int r) {
