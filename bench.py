@@ -97,6 +97,8 @@ def parse():
                          "each back to back for a few seconds with power and clocks sampled")
     ap.add_argument("--skip-split", action="store_true",
                     help="omit the split key-list and external-contribution measurements")
+    ap.add_argument("--skip-queued", action="store_true",
+                    help="omit the work-queue forward (ba_att_forward_queued) timed against the one-tile forward")
     ap.add_argument("--skip-sweep", action="store_true",
                     help="omit the long-context sweep (16K tokens, block 64/128, sparsity 0/50/75%%)")
     ap.add_argument("--skip-quality", action="store_true",
@@ -718,6 +720,19 @@ class Problem:
                                             o.data_ptr(), self.code if code is None else code,
                                             self.lse.data_ptr(), self.sptr))
 
+    def sparse_queued(self, o=None, lse=None):
+        """The same forward through ba_att_forward_queued (resident grid, per-XCD work queues)."""
+        import torch
+        B, H, N, D, blk = self.dims
+        if getattr(self, "queue", None) is None:
+            self.queue = torch.zeros(16, dtype=torch.int32, device=self.q.device)
+        o = self.o if o is None else o
+        lse = self.lse if lse is None else lse
+        self._check(self.lib.ba_att_forward_queued(B, H, N, D, blk, 0.0, self.q.data_ptr(), self.k.data_ptr(),
+                                                   self.v.data_ptr(), self.idx.data_ptr(), self.cnt.data_ptr(),
+                                                   self.keep, o.data_ptr(), self.code, lse.data_ptr(),
+                                                   self.queue.data_ptr(), self.sptr))
+
     def dense(self):
         B, H, N, D, blk = self.dims
         self._check(self.lib.ba_att_dense(B, H, N, D, 0.0, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
@@ -726,6 +741,34 @@ class Problem:
     def label(self) -> str:
         B, H, N, D, blk = self.dims
         return f"B{B} H{H} N{N} D{D} b{blk}"
+
+
+def queued_measurement(p, stream, warmup: int, steps: int, rounds: int = 3) -> dict:
+    """ba_att_forward_queued against ba_att_forward on a workload's own block
+    lists: outputs compared bit for bit, then the select + sparse step timed
+    both ways (back to back, alternating rounds so that clock drift falls on
+    both), and each sparse kernel alone between event pairs."""
+    import numpy as np
+    import torch
+    p.select()
+    o2, l2 = torch.empty_like(p.o), torch.empty_like(p.lse)
+    p.sparse()
+    p.sparse_queued(o2, l2)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o2, p.o) and torch.equal(l2, p.lse))
+    del o2, l2
+    plain, queued, k_plain, k_queued = [], [], [], []
+    for _ in range(rounds):
+        plain.append(time_steps(p.select, p.sparse, stream, warmup, steps)[0])
+        queued.append(time_steps(p.select, p.sparse_queued, stream, warmup, steps)[0])
+        k_plain.append(time_calls(p.sparse, stream, 2, steps))
+        k_queued.append(time_calls(p.sparse_queued, stream, 2, steps))
+    t0, t1 = float(np.median(plain)), float(np.median(queued))
+    return {"workload": p.w.name, "shape": p.label(), "bit_identical": same,
+            "step_ms": round(t0, 5), "step_ms_queued": round(t1, 5), "step_speedup": round(t0 / t1, 4),
+            "speedup_vs_dense_queued": None,
+            "sparse_ms": round(float(np.median(k_plain)), 5), "sparse_ms_queued": round(float(np.median(k_queued)), 5),
+            "rounds": rounds, "steps_per_round": steps}
 
 
 def secondary(lib, name: str, args, dev, stream, flush, sink) -> dict:
@@ -741,6 +784,9 @@ def secondary(lib, name: str, args, dev, stream, flush, sink) -> dict:
     dense_ms = time_calls(p.dense, stream, max(5, args.warmup // 2), max(5, args.steps // 2))
     kept = kept_tile_flops(p.mask.cpu().numpy(), p.w.N, p.w.D, p.w.block)
     spa_ms, selm = float(spa_t.mean()), float(np.median(sel_f))
+    qd = None if args.skip_queued else queued_measurement(p, stream, max(5, args.warmup // 2), args.steps)
+    if qd is not None:
+        qd["speedup_vs_dense_queued"] = round(dense_ms / qd["step_ms_queued"], 4)
     res = {"workload": p.w.description, "name": name, "shape": p.label(), "sparsity": p.sp,
            "keep": p.keep, "n_blocks": p.n, "ms_per_step": round(step_ms, 5),
            "dense_equiv_tflops": round(p.dense_flops / step_ms / 1e9, 2),
@@ -748,7 +794,8 @@ def secondary(lib, name: str, args, dev, stream, flush, sink) -> dict:
            "select_ms": round(float(sel_t.mean()), 5), "sparse_attention_ms": round(spa_ms, 5),
            "sparse_frac_of_mfma_peak": round(kept / (spa_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
            "select_flushed_ms": round(selm, 5),
-           "select_frac_of_hbm_peak": round(p.sel_bytes / (selm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+           "select_frac_of_hbm_peak": round(p.sel_bytes / (selm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "queued": qd}
     del p
     torch.cuda.empty_cache()
     return res
@@ -862,6 +909,13 @@ def main():
                                         (P.q, P.k, P.v, P.idx, P.cnt, P.o, P.lse), 10, max(5, args.steps // 2))
         print(f"[bench] external contribution: {external}", file=sys.stderr, flush=True)
 
+    queued = None
+    if not args.skip_queued:
+        queued = queued_measurement(P, stream, max(5, args.warmup // 2), args.steps)
+        if dense_ms:
+            queued["speedup_vs_dense_queued"] = round(dense_ms / queued["step_ms_queued"], 4)
+        print(f"[bench] work-queue forward: {queued}", file=sys.stderr, flush=True)
+
     quality = None
     if not args.skip_quality:
         from block_sparse_attention_ba_amd import quality as qmod
@@ -942,6 +996,7 @@ def main():
         "measured_peaks": peaks,
         "split_kv": split_kv,
         "external": external,
+        "queued": queued,
         "power": power,
         "operand_data": opdata,
         "selection_quality": quality,

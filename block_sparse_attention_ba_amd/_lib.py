@@ -24,6 +24,8 @@ SIGNATURES = [
     ("ba_att_mask_to_index", ctypes.c_int, [_i32, _i32, _i32, _p, _i32, _p, _p, _p]),
     ("ba_att_forward", ctypes.c_int,
      [_i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p]),
+    ("ba_att_forward_queued", ctypes.c_int,
+     [_i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p]),
     ("ba_att_forward_split_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
     ("ba_att_forward_split_parts", _i32, [_i32, _i32, _i32, _i32, _i32]),
     ("ba_att_forward_split", ctypes.c_int,

@@ -200,6 +200,45 @@ def forward(q, k, v, idx, cnt, block: int, scale: float | None = None,
     return out, lse
 
 
+QUEUE_WORDS = 16  # BA_ATT_QUEUE_WORDS
+_queues: dict = {}
+
+
+def queue_for(device: torch.device, stream_handle: int) -> torch.Tensor:
+    """The zeroed work queue kept for one (device, stream): the kernel leaves
+    it zero at its end, so one queue serves every call on that stream."""
+    key = (device.index, int(stream_handle))
+    qt = _queues.get(key)
+    if qt is None:
+        qt = torch.zeros(QUEUE_WORDS, dtype=torch.int32, device=device)
+        _queues[key] = qt
+    return qt
+
+
+def forward_queued(q, k, v, idx, cnt, block: int, scale: float | None = None,
+                   out_dtype: torch.dtype = torch.float32, out=None, lse=None, return_lse: bool = True,
+                   queue: torch.Tensor | None = None):
+    """ba_att_forward_queued: the sparse forward with its tiles taken from a
+    per-XCD work queue by a resident grid; same results as forward(), bit for
+    bit.  queue: int32 [16] zeros (default: one kept per device and stream)."""
+    B, H, N, D = _forward_args(q, k, v, idx, cnt, block)
+    out, lse, code = _out(q, out_dtype, out, lse, return_lse)
+    with _on(q):
+        stream = _stream(q)
+        if queue is None:
+            queue = queue_for(q.device, stream or 0)
+        else:
+            _need(queue, "queue", torch.int32, 1, q.device)
+            if queue.numel() < QUEUE_WORDS or queue.data_ptr() % 64:
+                raise ValueError("queue must hold 16 int32 words, 64-byte aligned")
+        _check(_lib.load().ba_att_forward_queued(B, H, N, D, block, float(scale or 0.0), q.data_ptr(),
+                                                 k.data_ptr(), v.data_ptr(), idx.data_ptr(), cnt.data_ptr(),
+                                                 int(idx.shape[3]), out.data_ptr(), code,
+                                                 lse.data_ptr() if lse is not None else None,
+                                                 queue.data_ptr(), stream))
+    return out, lse
+
+
 def _forward_args(q, k, v, idx, cnt, block):
     B, H, N, D = _qkv_shape(q)
     for name, t in (("k", k), ("v", v)):

@@ -131,8 +131,20 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint8_t* dst
                                              16, voff[j], 0, 0, 0);
 }
 
-template <int D, int WAVES, int BLK, bool SPARSE, bool OUT_F32>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
+// LDS bytes of one K or V tile (64 keys of D bf16 values)
+template <int D>
+constexpr int attn_tile_bytes() { return kChunk * D * 2; }
+
+// One tile of the forward: query tile `logical` (tile-major, then key-list
+// part) of the launch described by p, with the workgroup's K and V LDS tiles.
+// Every wave of the workgroup calls it with the same `logical`; tid is the
+// thread's index in the workgroup.
+// REMAT: which of the lane's addresses are formed again in every chunk
+// instead of held across the chunk loop (fewer live registers): bit 0 the
+// tile-copy offsets, bit 1 the K operand reads, bit 2 the V operand reads.
+template <int D, int WAVES, int BLK, bool SPARSE, bool OUT_F32, int REMAT = 0>
+__device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, uint8_t* Ktile,
+                                          uint8_t* Vtile) {
   constexpr int ROWS = WAVES * 32;
   constexpr int KSTEPS = D / 16;          // MFMA k-steps of the score product
   constexpr int DT = D / 32;              // 32-wide d tiles of the output
@@ -146,22 +158,16 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   static_assert(!SPARSE || ROWS == BLK || PAIR, "sparse tile must be one or two query blocks");
   static_assert((kChunk * CPR) % (64 * WAVES) == 0, "tile must split evenly over the waves");
 
-  // two separate arrays: the compiler then sees that a copy into one does not
-  // write the other, and does not make the reads of V wait for the copy of K
-  __shared__ __attribute__((aligned(1024))) uint8_t Ktile[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vtile[TILE_BYTES];
   uint8_t* const Kbuf = Ktile;
   uint8_t* const Vbuf = Vtile;
 
-  const int logical = xcd_remap(blockIdx.x, p.total);
-  if (logical < 0) return;
   const int tile = logical / p.n_split;      // the parts of a tile are neighbours
   const int part = logical - tile * p.n_split;
   const int bh = tile / p.n_qtiles;
   const int qt = tile - bh * p.n_qtiles;
   const int N = p.N;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;    // lane half
   const int lq = lane & 31;   // query column of this lane
 
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
       // the packed words, padded to whole 16-byte groups with all-ones words,
       // which are above every word and add to no rank
       const int tot4 = (tot + 3) >> 2;
-      for (int e = threadIdx.x; e < 4 * tot4; e += T) {
+      for (int e = tid; e < 4 * tot4; e += T) {
         uint32_t w = 0xFFFFFFFFu;
         if (e < tot) {
           const bool inB = e >= cA;
@@ -262,7 +268,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
       // rank = number of smaller words; every lane reads the same 16 bytes
       // (a broadcast), several in flight
       const u32x4* const keys4 = reinterpret_cast<const u32x4*>(keys);
-      for (int e = threadIdx.x; e < tot; e += T) {
+      for (int e = tid; e < tot; e += T) {
         const uint32_t v = keys[e];
         int rank = 0;
 #pragma unroll 4
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
         return !((v >> 16) == (u >> 16) && ((v >> 15) & 1u) && !((u >> 15) & 1u));
       };
       const int seg = (tot + T - 1) / T;
-      const int s0 = min(tot, (int)threadIdx.x * seg), s1 = min(tot, s0 + seg);
+      const int s0 = min(tot, (int)tid * seg), s1 = min(tot, s0 + seg);
       int mine_starts = 0;
       for (int r = s0; r < s1; ++r) mine_starts += starts(r);
       // exclusive scan of the per-thread counts: within each wave by lane
@@ -347,14 +353,40 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
   // p = (j*WAVES + wave)*64 + lane (16 bytes) of copy j; the slot holds
   // logical chunk c of row r under the tile's swizzle.  Byte offsets of the
   // source chunks are loop-invariant.
-  uint32_t voff_k[DMA], voff_v[DMA];
+  // (lane_c is the lane index these addresses are formed from: with REMAT
+  // it is made opaque in every chunk, so they are formed again there)
+  int lane_c = lane;   // copy offsets
+  int lane_k = lane;   // K operand reads
+  int lane_v = lane;   // V operand reads
+  auto copy_offsets = [&](uint32_t* vk, uint32_t* vv) {
 #pragma unroll
-  for (int j = 0; j < DMA; ++j) {
-    const int slot = (j * WAVES + wave) * 64 + lane;
-    const int r = slot / CPR, s = slot % CPR;
-    voff_k[j] = r * ROW_BYTES + k_slot<CPR>(r, s) * 16;
-    voff_v[j] = r * ROW_BYTES + v_slot<CPR>(r, s) * 16;
-  }
+    for (int j = 0; j < DMA; ++j) {
+      const int slot = (j * WAVES + wave) * 64 + lane_c;
+      const int r = slot / CPR, s = slot % CPR;
+      if (vk) vk[j] = r * ROW_BYTES + k_slot<CPR>(r, s) * 16;
+      if (vv) vv[j] = r * ROW_BYTES + v_slot<CPR>(r, s) * 16;
+    }
+  };
+  uint32_t voff_k[DMA], voff_v[DMA];
+  copy_offsets(voff_k, voff_v);
+  auto copy_k = [&](const __amdgpu_buffer_rsrc_t& rs) {
+    if constexpr ((REMAT & 1) != 0) {
+      uint32_t vo[DMA];
+      copy_offsets(vo, nullptr);
+      dma_tile<DMA, WAVES>(rs, Kbuf, wave, vo);
+    } else {
+      dma_tile<DMA, WAVES>(rs, Kbuf, wave, voff_k);
+    }
+  };
+  auto copy_v = [&](const __amdgpu_buffer_rsrc_t& rs) {
+    if constexpr ((REMAT & 1) != 0) {
+      uint32_t vo[DMA];
+      copy_offsets(nullptr, vo);
+      dma_tile<DMA, WAVES>(rs, Vbuf, wave, vo);
+    } else {
+      dma_tile<DMA, WAVES>(rs, Vbuf, wave, voff_v);
+    }
+  };
   auto tile_rsrc = [&](const uint16_t* src, int k0) {
     // (a chunk may start past N: the second half of a 128-key tail block with
     // at most 64 rows; its count must clamp at 0, as a negative count would
@@ -369,15 +401,15 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
   // ---- LDS operand reads
   auto read_k = [&](int kt, int ks) -> bf16x8 {  // A of S^T: key kt*32+lq, d = 16ks+8g..+8
-    const int r = kt * 32 + lq;
-    return *reinterpret_cast<const bf16x8*>(Kbuf + r * ROW_BYTES + k_slot<CPR>(r, ks * 2 + g) * 16);
+    const int r = kt * 32 + (lane_k & 31);
+    return *reinterpret_cast<const bf16x8*>(Kbuf + r * ROW_BYTES + k_slot<CPR>(r, ks * 2 + (lane_k >> 5)) * 16);
   };
   // A of O^T for d tile `dtile`, keys base+4g+{0..3} and base+8+4g+{0..3},
   // base = 16*step: two transposing reads of the row-major V tile
-  const int grp = lane >> 4, li = lane & 15;
-  const int dl = 16 * (grp & 1) + 4 * (li & 3);  // d of this lane's 8-byte read
-  const int kr = 4 * (grp >> 1) + (li >> 2);      // key row of this lane's read within a step
   auto read_v = [&](int step, int dtile) -> bf16x8 {
+    const int grp = lane_v >> 4, li = lane_v & 15;
+    const int dl = 16 * (grp & 1) + 4 * (li & 3);  // d of this lane's 8-byte read
+    const int kr = 4 * (grp >> 1) + (li >> 2);      // key row of this lane's read within a step
     const int dd = dtile * 32 + dl;
     const int r0 = step * 16 + kr, r1 = r0 + 8;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -404,9 +436,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
   int own_next = 0;
   int k0_next = c_begin < c_end ? chunk_entry(c_begin, own_next) : 0;
-  if (c_begin < c_end) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
+  if (c_begin < c_end) copy_k(tile_rsrc(Kh, k0_next));
 
   for (int c = c_begin; c < c_end; ++c) {
+    if constexpr ((REMAT & 1) != 0) __asm__ volatile("" : "+v"(lane_c));
+    if constexpr ((REMAT & 2) != 0) __asm__ volatile("" : "+v"(lane_k));
+    if constexpr ((REMAT & 4) != 0) __asm__ volatile("" : "+v"(lane_v));
     const int k0 = k0_next;
     // in a pair, a wave works only on the blocks its own query block keeps;
     // it still copies its share of every tile and meets every barrier
@@ -416,7 +451,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(c) landed
     __syncthreads();  // K(c) visible to all waves; every wave is done with V(c-1)
-    dma_tile<DMA, WAVES>(tile_rsrc(Vh, k0), Vbuf, wave, voff_v);
+    copy_v(tile_rsrc(Vh, k0));
 
     bf16x8 pf[4];  // P^T operand of each 16-key step
     if (mine) {
@@ -438,14 +473,15 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
         }
       }
       // keys past the end of the sequence (or of a skipped entry)
+      // (key kt*32 + 8(r/4) + 4g + r%4 is past the end when its constant part
+      // reaches valid - 4g: one register per chunk, not one per key)
       if (valid < kChunk) {
+        const int lim = valid - 4 * g;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= valid) sacc[kt][r] = -__builtin_inff();
-          }
+          for (int r = 0; r < 16; ++r)
+            if (kt * 32 + 8 * (r >> 2) + (r & 3) >= lim) sacc[kt][r] = -__builtin_inff();
       }
       // two chains of three-input maxima (v_max3_f32): 17 instructions for 32 values
       float ma = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
@@ -497,7 +533,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V(c) landed
     __syncthreads();  // V(c) visible; every wave is done with K(c)
-    if (c + 1 < c_end) dma_tile<DMA, WAVES>(tile_rsrc(Kh, k0_next), Kbuf, wave, voff_k);
+    if (c + 1 < c_end) copy_k(tile_rsrc(Kh, k0_next));
 
     if (!mine) continue;
     // O^T (D x 32 queries) += V^T P^T, V operands read one step ahead
@@ -563,6 +599,85 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
           *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + part * p.o_part_stride + row * D + dd) = w;
         }
       }
+  }
+}
+
+template <int D, int WAVES, int BLK, bool SPARSE, bool OUT_F32>
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
+  // two separate arrays: the compiler then sees that a copy into one does not
+  // write the other, and does not make the reads of V wait for the copy of K
+  __shared__ __attribute__((aligned(1024))) uint8_t Ktile[attn_tile_bytes<D>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vtile[attn_tile_bytes<D>()];
+  const int logical = xcd_remap(blockIdx.x, p.total);
+  if (logical < 0) return;
+  attn_tile<D, WAVES, BLK, SPARSE, OUT_F32>(p, logical, threadIdx.x, Ktile, Vtile);
+}
+
+// ---------------------------------------------------------------------------
+// Work-queue form of the sparse forward.  The grid holds only as many
+// workgroups as the device keeps resident; each takes query tiles from a
+// queue until none is left.  The tiles are dealt into one queue per XCD, a
+// contiguous range in head order (the ranges xcd_remap gives the one-tile
+// launch), so the workgroups of an XCD share its L2 as before.  A workgroup
+// whose own queue is empty takes tiles from the other XCDs' queues, so an
+// XCD that runs faster (the XCDs' clocks differ under the power limit) or
+// draws cheaper tiles (pair tiles walk unions of different sizes) ends with
+// the others instead of idling while they drain.
+//
+// queue: kQueueWords words, zero when the launch starts.  Words 0..7 count
+// the tickets drawn from each XCD's range, word 8 the workgroups that have
+// left the loop; the last workgroup to leave sets them back to zero, so the
+// same queue serves the next launch on the stream.
+// ---------------------------------------------------------------------------
+constexpr int kQueueWords = 16;
+// The loop keeps the tile code's state live across tiles, so the K operand
+// addresses are formed in every chunk: the kernel then fits the 168 VGPRs
+// of three waves per SIMD, as the one-tile kernel does, with its few spills
+// outside the chunk loop.
+constexpr int kQueuedRemat = 2;
+
+template <int D, int WAVES, int BLK, bool OUT_F32>
+__global__ __launch_bounds__(WAVES * 64, 3) void attn_fwd_queued_kernel(AttnParams p, uint32_t* queue) {
+  __shared__ __attribute__((aligned(1024))) uint8_t Ktile[attn_tile_bytes<D>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vtile[attn_tile_bytes<D>()];
+  // next tile, in a slot per iteration parity: a slot is rewritten two
+  // iterations later, after a barrier every wave passes once it has read it
+  __shared__ int next_tile[2];
+  const int xcd = blockIdx.x % kNumXcd;  // workgroups are dealt round-robin over the XCDs
+  const int per = (p.total + kNumXcd - 1) / kNumXcd;
+  uint32_t open = (1u << kNumXcd) - 1;  // queues this workgroup has not yet found empty
+  for (int it = 0;; ++it) {
+    if (threadIdx.x == 0) {
+      int t = -1;
+      for (int i = 0; i < kNumXcd && t < 0; ++i) {
+        const int y = (xcd + i) % kNumXcd;
+        if (!((open >> y) & 1u)) continue;
+        const int lo = y * per;
+        const int len = min(per, p.total - lo);
+        const uint32_t ticket = len > 0 ? atomicAdd(&queue[y], 1u) : 0xFFFFFFFFu;
+        if (len > 0 && ticket < (uint32_t)len) t = lo + (int)ticket;
+        else open &= ~(1u << y);
+      }
+      next_tile[it & 1] = t;
+    }
+    __syncthreads();
+    const int logical = __builtin_amdgcn_readfirstlane(next_tile[it & 1]);
+    if (logical < 0) break;  // uniform: every wave read the same slot
+    // the thread index, opaque to the compiler in each iteration: values
+    // derived from it are then formed inside each tile as in the one-tile
+    // kernel, not hoisted out of this loop and held live across every tile
+    int tid = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid));
+    attn_tile<D, WAVES, BLK, true, OUT_F32, kQueuedRemat>(p, logical, tid, Ktile, Vtile);
+  }
+  if (threadIdx.x == 0) {
+    // every ticket this workgroup draws precedes its count of leaving
+    const uint32_t left =
+        __hip_atomic_fetch_add(&queue[kNumXcd], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == gridDim.x - 1) {
+      for (int i = 0; i <= kNumXcd; ++i)
+        __hip_atomic_store(&queue[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <math.h>
 #include <mutex>
 #include <stdint.h>
@@ -147,6 +148,32 @@ void launch_attn(const ba::AttnParams& p, bool out_f32, hipStream_t s) {
     ba::attn_fwd_kernel<D, WAVES, BLK, SPARSE, true><<<grid, WAVES * 64, 0, s>>>(p);
   else
     ba::attn_fwd_kernel<D, WAVES, BLK, SPARSE, false><<<grid, WAVES * 64, 0, s>>>(p);
+}
+
+// Work-queue sparse forward: as many workgroups as the device keeps
+// resident (a multiple of the XCD count), each taking tiles from the queue.
+template <int D, int WAVES, int BLK, bool OUT_F32>
+ba_status launch_attn_queued_t(const ba::AttnParams& p, uint32_t* queue, hipStream_t s) {
+  auto kern = ba::attn_fwd_queued_kernel<D, WAVES, BLK, OUT_F32>;
+  // resident workgroups per compute unit, asked once (a property of the
+  // kernel's resources on this architecture)
+  static std::atomic<int> per_cu_cached{0};
+  int per_cu = per_cu_cached.load();
+  if (per_cu < 1) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WAVES * 64, 0) != hipSuccess || per_cu < 1)
+      return BA_ERR_HIP;
+    per_cu_cached.store(per_cu);
+  }
+  const long long resident = (long long)device_cus() * per_cu / ba::kNumXcd * ba::kNumXcd;
+  const long long wgs = std::max<long long>(ba::kNumXcd, std::min<long long>(resident, round_up8(p.total)));
+  kern<<<dim3((unsigned)wgs), WAVES * 64, 0, s>>>(p, queue);
+  return BA_OK;
+}
+
+template <int D, int WAVES, int BLK>
+ba_status launch_attn_queued(const ba::AttnParams& p, bool out_f32, uint32_t* queue, hipStream_t s) {
+  return out_f32 ? launch_attn_queued_t<D, WAVES, BLK, true>(p, queue, s)
+                 : launch_attn_queued_t<D, WAVES, BLK, false>(p, queue, s);
 }
 
 // Workspace of the selection pass: the pooled statistics aq, ak (fp32
@@ -304,6 +331,7 @@ constexpr int kMaxSplit = 64;
 // 15 bits with 0x7FFF for an invalid one, so every block index must fit in
 // 15 bits below 0x7FFF.
 static_assert(kMaxN / 64 < 0x7FFF, "block indices of the walk fit 15 bits");
+static_assert(BA_ATT_QUEUE_WORDS == ba::kQueueWords, "queue size in the header and the kernel agree");
 
 // Multiplier of the sparse walk order: the integer nearest n/phi (phi the
 // golden ratio) that is coprime with n, so that J -> J*g mod n permutes the
@@ -354,7 +382,7 @@ ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t blo
                          const void* q, const void* k, const void* v, const int32_t* block_idx,
                          const int32_t* block_cnt, int32_t max_keep, int n_split, void* o, bool o_f32,
                          float* lse, size_t o_stride, size_t lse_stride, const float* o_ext,
-                         const float* lse_ext, hipStream_t s) {
+                         const float* lse_ext, hipStream_t s, uint32_t* queue = nullptr) {
   const int n = num_blocks(N, block);
   // block 128: one four-wave tile per query block; block 64: one four-wave
   // tile per pair of neighbouring query blocks
@@ -382,6 +410,15 @@ ba_status launch_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t blo
   p.lse_ext = lse_ext;
   p.walk_mul = walk_multiplier(n);
   p.walk_inv = walk_inverse(p.walk_mul, n);
+  if (queue != nullptr) {
+    ba_status st;
+    if (D == 128) st = block == 64 ? launch_attn_queued<128, 4, 64>(p, o_f32, queue, s)
+                                   : launch_attn_queued<128, 4, 128>(p, o_f32, queue, s);
+    else st = block == 64 ? launch_attn_queued<64, 4, 64>(p, o_f32, queue, s)
+                          : launch_attn_queued<64, 4, 128>(p, o_f32, queue, s);
+    if (st != BA_OK) return st;
+    return finish_launch();
+  }
   if (D == 128) {
     if (block == 64) launch_attn<128, 4, 64, true>(p, o_f32, s);
     else launch_attn<128, 4, 128, true>(p, o_f32, s);
@@ -422,6 +459,20 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
   if (!aligned(o, 16) || (lse && !aligned(lse, 4))) return BA_ERR_INVALID_ARG;
   return launch_forward(B, H, N, D, block, scale, q, k, v, block_idx, block_cnt, max_keep, 1, o,
                         o_dtype == BA_F32, lse, 0, 0, nullptr, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int ba_att_forward_queued(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                          const void* q, const void* k, const void* v, const int32_t* block_idx,
+                          const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
+                          float* lse, uint32_t* queue, void* stream) {
+  ba_status st = check_forward(B, H, N, D, block, q, k, v, block_idx, block_cnt, max_keep);
+  if (st != BA_OK) return st;
+  if (!o || (o_dtype != BA_BF16 && o_dtype != BA_F32)) return BA_ERR_INVALID_ARG;
+  if (!aligned(o, 16) || (lse && !aligned(lse, 4))) return BA_ERR_INVALID_ARG;
+  if (!queue || !aligned(queue, 64)) return BA_ERR_WORKSPACE;
+  return launch_forward(B, H, N, D, block, scale, q, k, v, block_idx, block_cnt, max_keep, 1, o,
+                        o_dtype == BA_F32, lse, 0, 0, nullptr, nullptr, static_cast<hipStream_t>(stream),
+                        queue);
 }
 
 size_t ba_att_forward_split_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t n_split) {

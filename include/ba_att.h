@@ -155,6 +155,33 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
                    const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
                    float* lse, void* stream);
 
+/* Words of the work queue of ba_att_forward_queued (64 bytes). */
+#define BA_ATT_QUEUE_WORDS 16
+
+/* ba_att_forward with its tiles dealt from a work queue: the persistent,
+ * XCD-aware form of the block-sparse attention pass (same operation, "The
+ * pith" of the review; the one-launch, persistent scheduling of the review's
+ * "lightweight" two-pass design is this library's).  The launch holds only
+ * the workgroups the device keeps resident; each takes query tiles from one
+ * queue per XCD (a contiguous range of tiles in head order, so an XCD's
+ * workgroups share its L2) and, once that is empty, from the other XCDs'
+ * queues, so XCDs that run faster or draw cheaper tiles take more of them.
+ * Every row is computed by the same code as in ba_att_forward, so results
+ * are bit-identical to ba_att_forward's.
+ *   queue  uint32 [BA_ATT_QUEUE_WORDS], device memory, 64-byte aligned,
+ *          caller-owned.  It must hold zeros when the call's kernel starts,
+ *          and the kernel leaves it zero when it ends: zero it once when it
+ *          is allocated, then reuse it for every call on one stream.  Calls
+ *          whose kernels can run at the same time (different streams) need
+ *          different queues; a queue that does not start at zero makes
+ *          tiles be skipped (their output rows are left unwritten).
+ *          NULL or misaligned: BA_ERR_WORKSPACE.
+ * Other arguments, checks and errors as in ba_att_forward. */
+int ba_att_forward_queued(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                          const void* q, const void* k, const void* v, const int32_t* block_idx,
+                          const int32_t* block_cnt, int32_t max_keep, void* o, int32_t o_dtype,
+                          float* lse, uint32_t* queue, void* stream);
+
 /* Split key lists (split-KV).  Every row's list of kept key blocks is cut
  * into n_split contiguous parts (1 <= n_split <= 64); each part is attended
  * by its own workgroup into fp32 partial results in the workspace, and the

@@ -126,6 +126,30 @@ def test_forward_and_dense_reject_before_launch(lib):
     assert dense(B=1 << 16, H=1 << 8) == 2  # too many elements
 
 
+def test_forward_queued_rejects_before_launch(lib):
+    def fwd(**kw):
+        a = dict(B=1, H=1, N=1024, D=128, block=64, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE,
+                 mk=8, o=FAKE, od=1, lse=None, queue=FAKE)
+        a.update(kw)
+        return lib.ba_att_forward_queued(a["B"], a["H"], a["N"], a["D"], a["block"], 0.0, a["q"], a["k"],
+                                         a["v"], a["idx"], a["cnt"], a["mk"], a["o"], a["od"], a["lse"],
+                                         a["queue"], None)
+
+    # the forward's own checks come first, then the queue's
+    assert fwd(v=None) == 1 and fwd(o=None) == 1 and fwd(od=7) == 1 and fwd(mk=0) == 1
+    assert fwd(D=80) == 2 and fwd(block=256) == 2
+    assert fwd(queue=None) == 3
+    assert fwd(queue=FAKE + 16) == 3  # not 64-byte aligned
+    assert fwd(queue=None, q=None) == 1
+
+
+def test_queue_words_agree_between_header_and_binding():
+    from block_sparse_attention_ba_amd import api
+    text = open(HEADER).read()
+    m = re.search(r"#define BA_ATT_QUEUE_WORDS (\d+)", text)
+    assert m and int(m.group(1)) == api.QUEUE_WORDS
+
+
 def test_split_merge_ext_reject_before_launch(lib):
     assert lib.ba_att_forward_split_workspace_bytes(1, 2, 100, 64, 3) == 3 * 2 * 100 * 65 * 4
     assert lib.ba_att_forward_split_workspace_bytes(1, 2, 100, 64, 0) == 0

@@ -9,6 +9,8 @@ benchmark times (same C-ABI calls, same shapes).
   tiny, LLaDA-8B-shaped and long-context workloads, a seeded subset of 8
   heads for the distribution-shift and video workloads.  The oracle runs
   head by head on the host's cores.
+* The work-queue forward (ba_att_forward_queued) equals the forward bit for
+  bit on every row, on the oracle's lists and on the GPU's own.
 * End to end: the GPU forward on the GPU's own block lists equals the
   forward on the oracle's lists bit for bit on every row whose mask row
   equals the oracle's (all rows except counted near-tie mismatches), so the
@@ -91,8 +93,15 @@ def test_fullsize_select_and_forward(gpu_lib, name, sp):
     o, lse = gpu_lib.forward(q, k, v, oidx, ocnt, blk, out_dtype=torch.float32)
     o16, _ = gpu_lib.forward(q, k, v, oidx, ocnt, blk, out_dtype=torch.bfloat16)
     o_own, lse_own = gpu_lib.forward(q, k, v, idx, cnt, blk, out_dtype=torch.float32)
+    oq, lseq = gpu_lib.forward_queued(q, k, v, oidx, ocnt, blk, out_dtype=torch.float32)
+    oq_own, lseq_own = gpu_lib.forward_queued(q, k, v, idx, cnt, blk, out_dtype=torch.float32)
     torch.cuda.synchronize()
     del q, k, v
+    # the queued launch: the same tiles through the same code, so every row equals
+    assert torch.equal(oq, o) and torch.equal(lseq, lse), "queued forward differs (oracle lists)"
+    assert torch.equal(oq_own, o_own) and torch.equal(lseq_own, lse_own), "queued forward differs (own lists)"
+    _log("  queued forward: bit-identical to the forward on every row (both lists)")
+    del oq, lseq, oq_own, lseq_own
 
     heads = parity_heads(name, B, H)
     g_o = o.cpu().numpy()

@@ -143,7 +143,10 @@ def test_forward_with_oracle_mask(gpu_lib, case):
     cnt = torch.from_numpy(ref["cnt"]).cuda()
     o, lse = gpu_lib.forward(to_dev(q), to_dev(k), to_dev(v), idx, cnt, block, out_dtype=torch.float32)
     o16, lse16 = gpu_lib.forward(to_dev(q), to_dev(k), to_dev(v), idx, cnt, block, out_dtype=torch.bfloat16)
+    oq, lseq = gpu_lib.forward_queued(to_dev(q), to_dev(k), to_dev(v), idx, cnt, block, out_dtype=torch.float32)
     torch.cuda.synchronize()
+    # the work-queue launch: same tiles, same code, same bits
+    assert torch.equal(oq, o) and torch.equal(lseq, lse)
     o, lse = o.cpu().numpy(), lse.cpu().numpy()
     o16 = o16.float().cpu().numpy()
     att = orc.attention_oracle(q, k, v, ref["mask"], block)
@@ -342,6 +345,8 @@ def _forward_case(gpu_lib, q, k, v, idx, cnt, block, paths):
         dt = torch.bfloat16 if name.endswith("bf16") else torch.float32
         if name.startswith("forward_split"):
             out[name] = gpu_lib.forward_split(*args, int(name.split("(")[1].split(")")[0]), out_dtype=dt)
+        elif name.startswith("forward_queued"):
+            out[name] = gpu_lib.forward_queued(*args, out_dtype=dt)
         else:
             out[name] = gpu_lib.forward(*args, out_dtype=dt)
     torch.cuda.synchronize()
@@ -372,7 +377,8 @@ def test_forward_pair_walks_keep_each_rows_multiset(gpu_lib):
         idx[0, 0, I, :len(lst)] = lst
         cnt[0, 0, I] = len(lst)
     res = _forward_case(gpu_lib, q, k, v, idx, cnt, block,
-                        ["forward f32", "forward bf16", "forward_split(2) f32", "forward_split(4) bf16"])
+                        ["forward f32", "forward bf16", "forward_split(2) f32", "forward_split(4) bf16",
+                         "forward_queued f32"])
     check_rows_against_lists(q, k, v, idx, cnt, block, max_keep, res)
 
 
@@ -392,7 +398,8 @@ def test_forward_lists_too_long_to_reorder(gpu_lib, block):
     idx[0, 0, 1, ::97] = -1
     idx[0, 0, 3, 5::89] = n
     cnt = np.array([[[2100, 2100, 700, 1000]]], np.int32)   # tiles of 4200 and 1700 entries at block 64
-    res = _forward_case(gpu_lib, q, k, v, idx, cnt, block, ["forward f32", "forward_split(3) f32"])
+    res = _forward_case(gpu_lib, q, k, v, idx, cnt, block, ["forward f32", "forward_split(3) f32",
+                                                            "forward_queued f32"])
     check_rows_against_lists(q, k, v, idx, cnt, block, max_keep, res)
 
 
@@ -410,7 +417,7 @@ def test_forward_tail_tile_too_short_for_its_walk(gpu_lib, block, keep):
     rng = np.random.default_rng(block * keep)
     idx = np.stack([rng.choice(n, size=keep, replace=False) for _ in range(n)])[None, None].astype(np.int32)
     cnt = np.full((B, H, n), keep, np.int32)
-    res = _forward_case(gpu_lib, q, k, v, idx, cnt, block, ["forward f32", "forward bf16"])
+    res = _forward_case(gpu_lib, q, k, v, idx, cnt, block, ["forward f32", "forward bf16", "forward_queued bf16"])
     check_rows_against_lists(q, k, v, idx, cnt, block, keep, res, blocks=[0, 1, n - 3, n - 2, n - 1])
 
 
@@ -419,7 +426,7 @@ def test_forward_tail_tile_too_short_for_its_walk(gpu_lib, block, keep):
 def test_degenerate_sequence_lengths(gpu_lib, N, D, block):
     """Sequences of one token, of less than one block, of exactly one block
     and of one block plus one token, through selection, forward, split
-    forward and dense, against the oracle."""
+    forward, work-queue forward and dense, against the oracle."""
     import torch
     B, H = 1, 2
     q, k, v = make_case(B, H, N, D, "normal", seed=N + D)
@@ -433,13 +440,14 @@ def test_degenerate_sequence_lengths(gpu_lib, N, D, block):
     oidx, ocnt = torch.from_numpy(ref["idx"]).cuda(), torch.from_numpy(ref["cnt"]).cuda()
     o, lse = gpu_lib.forward(Q, K, V, oidx, ocnt, block)
     os_, ls_ = gpu_lib.forward_split(Q, K, V, oidx, ocnt, block, 3)
+    oq, lq = gpu_lib.forward_queued(Q, K, V, oidx, ocnt, block)
     od, ld = gpu_lib.dense(Q, K, V)
     torch.cuda.synchronize()
     att = orc.attention_oracle(q, k, v, ref["mask"], block)
     scale = 1.0 / math.sqrt(D)
     for h in range(H):
         Oo, Lo = att[(0, h)]
-        for name, (go, gl) in {"forward": (o, lse), "split": (os_, ls_)}.items():
+        for name, (go, gl) in {"forward": (o, lse), "split": (os_, ls_), "queued": (oq, lq)}.items():
             assert max_abs(go[0, h].cpu().numpy(), Oo) <= O_TOL, (name, h)
             assert max_abs(gl[0, h].cpu().numpy(), Lo) <= LSE_TOL, (name, h)
         qq, kk, vv = (orc.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))

@@ -1,6 +1,7 @@
 """Seeded sweep of random block lists through the sparse forward: random
 shapes, lengths up to and past max_keep, repeated and out-of-range entries
-in any order, empty rows and negative counts.  At block 64 neighbouring rows
+in any order, empty rows and negative counts, through the forward, the split
+forward and the work-queue forward.  At block 64 neighbouring rows
 are walked as one tile (their lists merged with owner bits), so this sweep
 exercises the walk construction on lists the selection pass never emits.
 Every row is checked against textbook attention over exactly the multiset
@@ -60,5 +61,11 @@ def test_random_lists_through_the_forward(gpu_lib, seed):
     parts = 2 + seed % 4
     print(f"seed {seed}: B{B} H{H} N{N} D{D} block {block} max_keep {max_keep} split {parts}", flush=True)
     res = _forward_case(gpu_lib, q, k, v, idx, cnt, block,
-                        ["forward f32", "forward bf16", f"forward_split({parts}) f32", f"forward_split({parts}) bf16"])
+                        ["forward f32", "forward bf16", f"forward_split({parts}) f32", f"forward_split({parts}) bf16",
+                         "forward_queued f32", "forward_queued bf16"])
+    # the queued launch runs the forward's own code on every tile
+    for dt in ("f32", "bf16"):
+        import torch
+        assert torch.equal(res[f"forward_queued {dt}"][0], res[f"forward {dt}"][0]), (seed, dt)
+        assert torch.equal(res[f"forward_queued {dt}"][1], res[f"forward {dt}"][1]), (seed, dt)
     check_rows_against_lists(q, k, v, idx, cnt, block, max_keep, res)
