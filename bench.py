@@ -771,6 +771,65 @@ def queued_measurement(p, stream, warmup: int, steps: int, rounds: int = 3) -> d
             "rounds": rounds, "steps_per_round": steps}
 
 
+def uneven_lists_measurement(p, stream, reps: int, rounds: int = 3) -> dict:
+    """The one-tile and the work-queue forward on block lists whose length
+    grows with the head: head i of the B*H keeps n - floor(sp_i * n) blocks,
+    sp_i rising linearly from 0 (first head) to 0.875 (last), each row a
+    seeded random subset.  The one-tile launch deals each XCD a contiguous
+    range of heads, so the XCD holding the first heads holds the most work;
+    the queues let the others take part of it.  Outputs compared bit for bit."""
+    import numpy as np
+    import torch
+    B, H, N, D, blk = p.dims
+    n, BH = p.n, B * H
+    g = torch.Generator(device=p.q.device).manual_seed(20260521)
+    idx = torch.argsort(torch.rand((B, H, n, n), generator=g, device=p.q.device), dim=-1).to(torch.int32)
+    sp = 0.875 * np.arange(BH) / max(1, BH - 1)
+    keep_h = [n - int(np.floor(s * n + 1e-9)) for s in sp]
+    cnt = torch.tensor(keep_h, dtype=torch.int32, device=p.q.device).view(B, H, 1).expand(B, H, n).contiguous()
+    o2, l2 = torch.empty_like(p.o), torch.empty_like(p.lse)
+    if getattr(p, "queue", None) is None:
+        p.queue = torch.zeros(16, dtype=torch.int32, device=p.q.device)
+
+    def plain(o=None, lse=None):
+        o = p.o if o is None else o
+        lse = p.lse if lse is None else lse
+        p._check(p.lib.ba_att_forward(B, H, N, D, blk, 0.0, p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(),
+                                      idx.data_ptr(), cnt.data_ptr(), n, o.data_ptr(), p.code, lse.data_ptr(),
+                                      p.sptr))
+
+    def queued(o=None, lse=None):
+        o = p.o if o is None else o
+        lse = p.lse if lse is None else lse
+        p._check(p.lib.ba_att_forward_queued(B, H, N, D, blk, 0.0, p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(),
+                                             idx.data_ptr(), cnt.data_ptr(), n, o.data_ptr(), p.code,
+                                             lse.data_ptr(), p.queue.data_ptr(), p.sptr))
+
+    plain()
+    queued(o2, l2)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o2, p.o) and torch.equal(l2, p.lse))
+    del o2, l2
+    tp, tq = [], []
+    for _ in range(rounds):
+        tp.append(time_calls(plain, stream, 2, reps))
+        tq.append(time_calls(queued, stream, 2, reps))
+    # kept-tile FLOPs, 4*D*|I|*|J| per kept pair with the tail block at its true size
+    size = torch.full((n,), float(blk), device=p.q.device, dtype=torch.float64)
+    size[-1] = N - (n - 1) * blk
+    on = torch.arange(n, device=p.q.device).view(1, 1, 1, n) < cnt.unsqueeze(-1)
+    kj = (size[idx.long()] * on).sum(-1)                     # [B,H,n]: keys attended by a row of block I
+    flops = float(4.0 * D * (kj * size.view(1, 1, n)).sum())
+    t0, t1 = float(np.median(tp)), float(np.median(tq))
+    del idx, cnt, on, kj
+    return {"lists": "head i of B*H keeps n - floor(sp_i*n) blocks per row, sp_i = 0.875*i/(B*H-1); "
+                     "seeded random subsets",
+            "kept_tile_tflop": round(flops / 1e12, 4), "bit_identical": same, "forward_ms": round(t0, 5),
+            "forward_queued_ms": round(t1, 5), "speedup": round(t0 / t1, 4),
+            "forward_tflops": round(flops / (t0 * 1e-3) / 1e12, 1),
+            "forward_queued_tflops": round(flops / (t1 * 1e-3) / 1e12, 1), "rounds": rounds, "reps": reps}
+
+
 def secondary(lib, name: str, args, dev, stream, flush, sink) -> dict:
     """The step against the dense kernel on another workload: step time,
     per-kernel times, the sparse kernel's and the flushed select pass's
@@ -912,6 +971,7 @@ def main():
     queued = None
     if not args.skip_queued:
         queued = queued_measurement(P, stream, max(5, args.warmup // 2), args.steps)
+        queued["uneven_lists"] = uneven_lists_measurement(P, stream, max(5, args.steps // 5))
         if dense_ms:
             queued["speedup_vs_dense_queued"] = round(dense_ms / queued["step_ms_queued"], 4)
         print(f"[bench] work-queue forward: {queued}", file=sys.stderr, flush=True)

@@ -622,7 +622,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 // whose own queue is empty takes tiles from the other XCDs' queues, so an
 // XCD that runs faster (the XCDs' clocks differ under the power limit) or
 // draws cheaper tiles (pair tiles walk unions of different sizes) ends with
-// the others instead of idling while they drain.
+// the others instead of idling while they drain.  Running tiles back to back
+// in one workgroup costs a few percent against the one-tile launch, so the
+// queues pay off only where the XCDs' shares differ: lists whose kept counts
+// vary from head to head, not the selection pass's equal rows.
 //
 // queue: kQueueWords words, zero when the launch starts.  Words 0..7 count
 // the tickets drawn from each XCD's range, word 8 the workgroups that have

@@ -167,7 +167,10 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
  * workgroups share its L2) and, once that is empty, from the other XCDs'
  * queues, so XCDs that run faster or draw cheaper tiles take more of them.
  * Every row is computed by the same code as in ba_att_forward, so results
- * are bit-identical to ba_att_forward's.
+ * are bit-identical to ba_att_forward's.  ba_att_forward deals every XCD an
+ * equal range of heads, so it is the faster call when every row keeps the
+ * same number of blocks (ba_att_select's lists); this call is the faster
+ * one when the kept counts vary from head to head.
  *   queue  uint32 [BA_ATT_QUEUE_WORDS], device memory, 64-byte aligned,
  *          caller-owned.  It must hold zeros when the call's kernel starts,
  *          and the kernel leaves it zero when it ends: zero it once when it
