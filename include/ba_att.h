@@ -38,9 +38,12 @@
  *    BA_ERR_UNSUPPORTED.
  *  - Every pointer argument is a DEVICE pointer on the current HIP device,
  *    16-byte aligned (the mask, idx and cnt buffers 4-byte aligned), owned by
- *    the caller.  The library allocates nothing, keeps no state between
- *    calls and never synchronises the host: work is enqueued on `stream`
- *    (a hipStream_t; NULL = the null stream) and completes asynchronously.
+ *    the caller.  The library allocates nothing and never synchronises the
+ *    host: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and completes asynchronously.  Results depend on no state kept
+ *    between calls (the library caches only device properties, such as the
+ *    resident workgroups per compute unit of ba_att_forward_queued's kernel;
+ *    ba_att_select_noalloc's fixed scratch is described there).
  *  - Errors: every argument is checked on the host before anything is
  *    launched; a failed check returns a nonzero ba_status and enqueues
  *    nothing.  After the launches hipGetLastError() is checked and a launch
