@@ -735,7 +735,7 @@ const char* ba_att_status_string(int status) {
     case BA_OK: return "ok";
     case BA_ERR_INVALID_ARG: return "invalid argument";
     case BA_ERR_UNSUPPORTED: return "unsupported shape or size";
-    case BA_ERR_WORKSPACE: return "workspace missing or too small";
+    case BA_ERR_WORKSPACE: return "workspace or work queue missing, misaligned or too small";
     case BA_ERR_HIP: return "HIP launch failed";
     case BA_ERR_SCRATCH: return "shape needs more than the 64 MiB fixed scratch of ba_att_select_noalloc";
     default: return "unknown status";

@@ -64,7 +64,7 @@ typedef enum {
   BA_OK = 0,
   BA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, sparsity outside [0,1), misalignment */
   BA_ERR_UNSUPPORTED = 2, /* D or block outside the supported set, sizes too large */
-  BA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ba_att_select_workspace_bytes */
+  BA_ERR_WORKSPACE = 3,   /* workspace or work queue missing, misaligned or too small */
   BA_ERR_HIP = 4,         /* a HIP launch failed */
   BA_ERR_SCRATCH = 5      /* ba_att_select_noalloc: the shape needs more than its fixed scratch */
 } ba_status;
@@ -162,9 +162,9 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
 #define BA_ATT_QUEUE_WORDS 16
 
 /* ba_att_forward with its tiles dealt from a work queue: the persistent,
- * XCD-aware form of the block-sparse attention pass (same operation, "The
- * pith" of the review; the one-launch, persistent scheduling of the review's
- * "lightweight" two-pass design is this library's).  The launch holds only
+ * XCD-aware form of the block-sparse attention pass.  The operation is
+ * ba_att_forward's (review, "The pith": attention over the selected blocks
+ * only); the scheduling is this library's, not the pages'.  The launch holds only
  * the workgroups the device keeps resident; each takes query tiles from one
  * queue per XCD (a contiguous range of tiles in head order, so an XCD's
  * workgroups share its L2) and, once that is empty, from the other XCDs'

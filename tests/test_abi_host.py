@@ -70,7 +70,7 @@ def test_workspace_bytes(lib):
 
 def test_status_strings(lib):
     for code, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape or size"),
-                       (3, b"workspace missing or too small"), (4, b"HIP launch failed")):
+                       (3, b"workspace or work queue missing, misaligned or too small"), (4, b"HIP launch failed")):
         assert lib.ba_att_status_string(code) == text
 
 
