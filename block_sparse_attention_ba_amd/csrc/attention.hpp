@@ -120,6 +120,28 @@ __device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
   return v;
 }
 
+// Keys of the 64-key chunk starting at k0 that lie before the sequence end N
+// (0 for a skipped entry, k0 < 0), formed in the scalar unit: written as
+// min/max the compiler would form the clamp as a vector med3 of scalars and
+// read it back with readfirstlane, in every copy of every chunk.
+__device__ __forceinline__ int chunk_rows(int k0, int N) {
+  int r;
+  __asm__("s_sub_i32 %0, %1, %2\n\t"
+          "s_min_i32 %0, %0, %3\n\t"
+          "s_max_i32 %0, %0, 0\n\t"
+          "s_cmp_lt_i32 %2, 0\n\t"
+          "s_cselect_b32 %0, 0, %0"
+          : "=&s"(r)
+          : "s"(N), "s"(k0), "i"(kChunk)
+          : "scc");
+  return r;
+}
+__device__ __forceinline__ int chunk_first(int k0) {
+  int r;
+  __asm__("s_max_i32 %0, %1, 0" : "=s"(r) : "s"(k0) : "scc");
+  return r;
+}
+
 // Copy j of a 64-key tile: lane `lane` of wave `wave` fills LDS slot
 // (j*WAVES + wave)*64 + lane (16 bytes) from byte offset voff[j] of the tile.
 template <int DMA, int WAVES>
@@ -391,11 +413,10 @@ __device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, ui
     // (a chunk may start past N: the second half of a 128-key tail block with
     // at most 64 rows; its count must clamp at 0, as a negative count would
     // wrap to an unbounded resource)
-    // The values are wave-uniform, but the clamp is selected as a vector
-    // med3; readfirstlane puts them back in scalar registers, else every copy
-    // is wrapped in a loop that re-establishes a uniform resource.
-    const int rows = __builtin_amdgcn_readfirstlane(k0 < 0 ? 0 : max(0, min(kChunk, N - k0)));
-    const int first = __builtin_amdgcn_readfirstlane(k0 < 0 ? 0 : k0);
+    // (formed in scalar registers: a resource held in vector registers would
+    // wrap every copy in a loop that re-establishes a uniform resource)
+    const int rows = chunk_rows(k0, N);
+    const int first = chunk_first(k0);
     return make_rsrc(src + (size_t)first * D, rows * ROW_BYTES);
   };
 
@@ -425,7 +446,11 @@ __device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, ui
   f32x16 oacc[DT];
 #pragma unroll
   for (int d = 0; d < DT; ++d) oacc[d] = f32x16{};
-  float m_run = -__builtin_inff();
+  // running max (log2 units).  It starts at a finite floor below any score
+  // rather than -inf: a chunk whose keys are all masked (max -inf) leaves it,
+  // the first real maximum then rescales by exp2(floor - m) = 0 exactly as
+  // from -inf, and no chunk needs a test for an infinite max.
+  float m_run = -1e30f;
   float l_run = 0.f;
   const float sl2 = p.scale_log2;
 
@@ -446,7 +471,7 @@ __device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, ui
     // in a pair, a wave works only on the blocks its own query block keeps;
     // it still copies its share of every tile and meets every barrier
     const bool mine = !PAIR || (own_next & my_bit) != 0;
-    const int valid = k0 < 0 ? 0 : max(0, min(kChunk, N - k0));
+    const int valid = chunk_rows(k0, N);
     if (c + 1 < c_end) k0_next = chunk_entry(c + 1, own_next);
 
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(c) landed
@@ -495,17 +520,18 @@ __device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, ui
       mloc = pair_max(mloc) * sl2;
       if (__any(mloc > m_run)) {  // exact running max: a row's largest probability is 1
         const float m_new = fmaxf(m_run, mloc);
-        if (m_new != -__builtin_inff()) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
-          l_run *= alpha;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from the floor
+        l_run *= alpha;
 #pragma unroll
-          for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
-          m_run = m_new;
-        }
+        for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+        m_run = m_new;
       }
-      const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+      const float m_use = m_run;
 
-      float psum = 0.f;
+      // (the sum starts from the first pair: 0 + x is not folded away, as
+      // -0 + 0 would not be -0; every pair sum here is >= 0, so the bits
+      // are those of a sum started at 0)
+      float psum;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -515,7 +541,8 @@ __device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, ui
           for (int e = 0; e < 4; ++e) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s + 2 * e], sl2, -m_use));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s + 2 * e + 1], sl2, -m_use));
-            psum += p0 + p1;
+            if (kt == 0 && s == 0 && e == 0) psum = p0 + p1;
+            else psum += p0 + p1;
             w[e] = pack_bf16x2(p0, p1);
           }
           pf[2 * kt + s] = __builtin_bit_cast(bf16x8, w);
