@@ -657,7 +657,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_kernel(AttnParams p) {
 // queue: kQueueWords words, zero when the launch starts.  Words 0..7 count
 // the tickets drawn from each XCD's range, word 8 the workgroups that have
 // left the loop; the last workgroup to leave sets them back to zero, so the
-// same queue serves the next launch on the stream.
+// same queue serves the next launch on the stream.  Every draw increments a
+// counter, so a workgroup leaves after at most 8 failed draws whatever the
+// queue held; a queue not at zero only makes the results wrong (stale
+// tickets skip tiles, a stale leaver count clears the queue early and tiles
+// are drawn again), and every list entry read back is range-checked.
 // ---------------------------------------------------------------------------
 constexpr int kQueueWords = 16;
 // The loop keeps the tile code's state live across tiles, so the K operand

@@ -179,8 +179,10 @@ int ba_att_forward(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, fl
  *          and the kernel leaves it zero when it ends: zero it once when it
  *          is allocated, then reuse it for every call on one stream.  Calls
  *          whose kernels can run at the same time (different streams) need
- *          different queues; a queue that does not start at zero makes
- *          tiles be skipped (their output rows are left unwritten).
+ *          different queues.  A queue that does not start at zero leaves
+ *          the results undefined (tiles skipped, or computed twice by
+ *          workgroups that race on their output rows); the launch still
+ *          ends and stays within the buffers.
  *          NULL or misaligned: BA_ERR_WORKSPACE.
  * Other arguments, checks and errors as in ba_att_forward. */
 int ba_att_forward_queued(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, float scale,
