@@ -449,7 +449,9 @@ __device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, ui
   // running max (log2 units).  It starts at a finite floor below any score
   // rather than -inf: a chunk whose keys are all masked (max -inf) leaves it,
   // the first real maximum then rescales by exp2(floor - m) = 0 exactly as
-  // from -inf, and no chunk needs a test for an infinite max.
+  // from -inf, and no chunk needs a test for an infinite max.  (A row whose
+  // scores all lie below the floor, which takes inputs whose products
+  // overflow fp32, would count as empty.)
   float m_run = -1e30f;
   float l_run = 0.f;
   const float sl2 = p.scale_log2;
