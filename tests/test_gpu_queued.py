@@ -23,6 +23,13 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _normal_qkv(B, H, N, D, seed):
+    """Seeded bf16 Q, K, V ~ N(0, 1) drawn on the GPU."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return tuple(torch.randn((B, H, N, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+
+
 def _lists(B, H, N, block, sp, seed):
     """Seeded random kept-block lists of the selection's shape (keep per row)."""
     n = orc.num_blocks(N, block)
@@ -56,7 +63,7 @@ def test_consecutive_calls_on_one_queue(gpu_lib):
     queue = torch.zeros(gpu_lib.QUEUE_WORDS, dtype=torch.int32, device="cuda")
     B, H, N, D, block = 1, 32, 8192 - 40, 128, 64
     _log(f"large: B{B} H{H} N{N} D{D} block {block}")
-    q, k, v = (torch.randn(B, H, N, D, device="cuda").to(torch.bfloat16) for _ in range(3))
+    q, k, v = _normal_qkv(B, H, N, D, seed=101)
     idx, cnt = _lists(B, H, N, block, 0.5, seed=1)
     (o, lse), (oq, lq) = _run(gpu_lib, q, k, v, idx, cnt, block, queue=queue)
     assert _zero(queue)
@@ -95,7 +102,7 @@ def test_caller_queue_on_a_second_stream(gpu_lib):
     beside the library's queue of the default stream."""
     import torch
     B, H, N, D, block = 1, 8, 4096, 128, 128
-    q, k, v = (torch.randn(B, H, N, D, device="cuda").to(torch.bfloat16) for _ in range(3))
+    q, k, v = _normal_qkv(B, H, N, D, seed=102)
     idx, cnt = _lists(B, H, N, block, 0.75, seed=3)
     ref, _ = _run(gpu_lib, q, k, v, idx, cnt, block)
     side = torch.cuda.Stream()
@@ -115,7 +122,7 @@ def test_graph_replays(gpu_lib):
     equal to the eager result bit for bit."""
     import torch
     B, H, N, D, block = 1, 4, 2048 + 33, 64, 64
-    q, k, v = (torch.randn(B, H, N, D, device="cuda").to(torch.bfloat16) for _ in range(3))
+    q, k, v = _normal_qkv(B, H, N, D, seed=103)
     idx, cnt = _lists(B, H, N, block, 0.5, seed=4)
     I, C = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
     queue = torch.zeros(gpu_lib.QUEUE_WORDS, dtype=torch.int32, device="cuda")
