@@ -422,8 +422,19 @@ __device__ __forceinline__ void attn_tile(AttnParams p, int logical, int tid, ui
 
   // ---- LDS operand reads
   auto read_k = [&](int kt, int ks) -> bf16x8 {  // A of S^T: key kt*32+lq, d = 16ks+8g..+8
-    const int r = kt * 32 + (lane_k & 31);
-    return *reinterpret_cast<const bf16x8*>(Kbuf + r * ROW_BYTES + k_slot<CPR>(r, ks * 2 + (lane_k >> 5)) * 16);
+    if constexpr ((REMAT & 2) != 0 && CPR == 16) {
+      // Row r = kt*32 + lq holds chunk c at slot c ^ (lq & 15), so the read
+      // of chunk 2ks+g is at A ^ (32*ks) (+ 8192 for kt = 1), with
+      // A = 256*lq + 16*((lq & 15) ^ g): the XOR only flips bits 5-7, which
+      // the other terms of A leave clear (the tile is 1 KB aligned).  One
+      // lane constant and one XOR per k-step when addresses are re-formed.
+      const int lqk = lane_k & 31;
+      const int a = lqk * ROW_BYTES + (((lqk & 15) ^ (lane_k >> 5)) << 4);
+      return *reinterpret_cast<const bf16x8*>(Kbuf + kt * 32 * ROW_BYTES + (a ^ (ks << 5)));
+    } else {
+      const int r = kt * 32 + (lane_k & 31);
+      return *reinterpret_cast<const bf16x8*>(Kbuf + r * ROW_BYTES + k_slot<CPR>(r, ks * 2 + (lane_k >> 5)) * 16);
+    }
   };
   // A of O^T for d tile `dtile`, keys base+4g+{0..3} and base+8+4g+{0..3},
   // base = 16*step: two transposing reads of the row-major V tile
